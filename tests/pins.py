@@ -1,0 +1,207 @@
+"""Independent checks ("pins") of the CPU reference.
+
+Each check computes the expected value by a route that does not go through
+the reference's own formula, eq. (8) of J. Su, "Continuous Softmax Attention":
+
+* ``quadrature_row``  -- Gauss-Legendre integration of the defining integrals,
+  eq. (2) with the interpolation eq. (3) (Problem Statement);
+* ``simplified_row_mp`` -- eq. (10)-(11) (Assembly and Simplification) in
+  50-digit mpmath arithmetic;
+* closed forms derived from eq. (2): equal logits (trapezoid rule), a linear
+  ramp of keys and values, the copied sink at t = 1;
+* the Taylor expansion of the correction b, eq. (13) (Analysis of the
+  Result), taken to second order.
+
+Every function returns the maximum deviation so that mutation tests can
+assert that a planted mistake in the reference is caught.
+"""
+
+from __future__ import annotations
+
+import math
+
+import mpmath as mp
+import numpy as np
+
+_GL_X, _GL_W = np.polynomial.legendre.leggauss(48)
+_GL_S = 0.5 * (_GL_X + 1.0)   # nodes on [0, 1]
+_GL_W01 = 0.5 * _GL_W
+
+
+def quadrature_row(q_t, k_hat, v_hat, t):
+    """(o_t, lse_t) by integrating e^{q.k_s} and e^{q.k_s} v_s over [0, t].
+
+    k_s and v_s are built by linear interpolation (eq. (3)); each unit segment
+    is integrated with a 48-point Gauss-Legendre rule on a fine sub-grid.
+    """
+    num = np.zeros(v_hat.shape[1])
+    den = 0.0
+    terms = []
+    for i in range(1, t + 1):
+        for sub in range(4):  # 4 sub-intervals per unit segment
+            s_local = (sub + _GL_S) / 4.0          # position inside [i-1, i], 0..1
+            w = _GL_W01 / 4.0
+            k_s = (1.0 - s_local)[:, None] * k_hat[i - 1] + s_local[:, None] * k_hat[i]
+            v_s = (1.0 - s_local)[:, None] * v_hat[i - 1] + s_local[:, None] * v_hat[i]
+            terms.append((k_s @ q_t, w, v_s))
+    shift = max(float(x.max()) for x, _, _ in terms)
+    for logits, w, v_s in terms:
+        e = np.exp(logits - shift) * w
+        den += e.sum()
+        num += e @ v_s
+    return num / den, shift + math.log(den)
+
+
+def _phi2_mp(x):
+    if x == 0:
+        return mp.mpf(1) / 2
+    return (mp.exp(x) - 1 - x) / (x * x)
+
+
+def simplified_row_mp(q_t, k_hat, v_hat, t, dps=50):
+    """(o_t, lse_t) by eq. (10)-(11) in mpmath: weights e^{a_i + b_i}, i = 0..t."""
+    with mp.workdps(dps):
+        q = [mp.mpf(float(x)) for x in q_t]
+        a = [mp.fsum(mp.mpf(float(kk)) * qq for kk, qq in zip(k_hat[i], q)) for i in range(t + 1)]
+        eb = []
+        for i in range(t + 1):
+            s = mp.mpf(0)
+            if i >= 1:
+                s += _phi2_mp(a[i - 1] - a[i])
+            if i <= t - 1:
+                s += _phi2_mp(a[i + 1] - a[i])
+            eb.append(s)
+        wts = [mp.exp(a[i]) * eb[i] for i in range(t + 1)]
+        den = mp.fsum(wts)
+        o = [mp.fsum(wts[i] * mp.mpf(float(v_hat[i][c])) for i in range(t + 1)) / den
+             for c in range(v_hat.shape[1])]
+        return np.array([float(x) for x in o]), float(mp.log(den))
+
+
+def hat(q, k, v, k0, v0, b=0, h=0):
+    k_hat = np.concatenate([k0[b, h][None], k[b, h]], axis=0)
+    v_hat = np.concatenate([v0[b, h][None], v[b, h]], axis=0)
+    return q[b, h], k_hat, v_hat
+
+
+def random_case(seed, T=9, d=3, dv=4, scale=1.0, sink=True):
+    rng = np.random.default_rng(seed)
+    q = rng.standard_normal((1, 1, T, d)) * scale
+    k = rng.standard_normal((1, 1, T, d))
+    v = rng.standard_normal((1, 1, T, dv))
+    k0 = rng.standard_normal((1, 1, d)) if sink else np.zeros((1, 1, d))
+    v0 = rng.standard_normal((1, 1, dv)) if sink else np.zeros((1, 1, dv))
+    return q, k, v, k0, v0
+
+
+def dev_vs_quadrature(ref, seed=0, scale=1.0):
+    """Max |reference - quadrature| over all rows of a small random case."""
+    q, k, v, k0, v0 = random_case(seed, scale=scale)
+    o, lse = ref(q, k, v, k0, v0)
+    qq, kh, vh = hat(q, k, v, k0, v0)
+    worst = 0.0
+    for r in range(q.shape[2]):
+        oq, lq = quadrature_row(qq[r], kh, vh, r + 1)
+        worst = max(worst, float(np.abs(o[0, 0, r] - oq).max()), abs(float(lse[0, 0, r]) - lq))
+    return worst
+
+
+def dev_vs_simplified(ref, seed=1, scale=1.5):
+    """Max |reference - mpmath eq. (10)-(11)| over all rows of a small random case."""
+    q, k, v, k0, v0 = random_case(seed, T=8, scale=scale)
+    o, lse = ref(q, k, v, k0, v0)
+    qq, kh, vh = hat(q, k, v, k0, v0)
+    worst = 0.0
+    for r in range(q.shape[2]):
+        om, lm = simplified_row_mp(qq[r], kh, vh, r + 1)
+        worst = max(worst, float(np.abs(o[0, 0, r] - om).max()), abs(float(lse[0, 0, r]) - lm))
+    return worst
+
+
+def dev_trapezoid(ref, seed=2, T=7):
+    """Equal logits (q = 0): weights 1/2, 1, ..., 1, 1/2 and lse = ln t."""
+    _, k, v, k0, v0 = random_case(seed, T=T)
+    q = np.zeros((1, 1, T, k.shape[-1]))
+    o, lse = ref(q, k, v, k0, v0)
+    vh = np.concatenate([v0[0, 0][None], v[0, 0]], axis=0)
+    worst = 0.0
+    for r in range(T):
+        t = r + 1
+        expect = (0.5 * vh[0] + vh[1:t].sum(axis=0) + 0.5 * vh[t]) / t
+        worst = max(worst, float(np.abs(o[0, 0, r] - expect).max()), abs(float(lse[0, 0, r]) - math.log(t)))
+    return worst
+
+
+def dev_linear_ramp(ref, beta=0.7, T=6):
+    """k_i = i w, v_i = i c with k_0 = v_0 = 0: q.k_s = beta s, v_s = s c exactly.
+
+    o_t = c (e^{beta t}(beta t - 1) + 1) / (beta (e^{beta t} - 1)),
+    lse_t = ln((e^{beta t} - 1)/beta).
+    """
+    d, dv = 3, 2
+    w = np.array([0.3, -0.2, 0.5])
+    qv = w * (beta / float(w @ w))          # q . w = beta
+    c = np.array([1.5, -0.25])
+    pos = np.arange(1, T + 1, dtype=np.float64)
+    q = np.broadcast_to(qv, (1, 1, T, d)).copy()
+    k = (pos[:, None] * w[None, :])[None, None]
+    v = (pos[:, None] * c[None, :])[None, None]
+    o, lse = ref(q, k, v, np.zeros((1, 1, d)), np.zeros((1, 1, dv)))
+    worst = 0.0
+    for r in range(T):
+        t = r + 1
+        with mp.workdps(40):  # the closed forms cancel for small beta*t; evaluate them exactly
+            bt = mp.mpf(beta) * t
+            ratio = (mp.exp(bt) * (bt - 1) + 1) / (mp.mpf(beta) * mp.expm1(bt))
+            o_exp = c * float(ratio)
+            l_exp = float(mp.log(mp.expm1(bt) / mp.mpf(beta)))
+        worst = max(worst, float(np.abs(o[0, 0, r] - o_exp).max()), abs(float(lse[0, 0, r]) - l_exp))
+    return worst
+
+
+def implied_b(ref, q_t, k_hat, t):
+    """Correction b_{t,i} recovered from the reference with one-hot values.
+
+    With v_i = e_i (the i-th unit vector, i = 0..t) the output is the vector of
+    normalised weights e^{a_i + b_i - lse}; so b_i = ln o_i + lse - a_i.
+    """
+    d = q_t.shape[0]
+    q = q_t[None, None, None, :].repeat(t, axis=2)
+    k = k_hat[1 : t + 1][None, None]
+    eye = np.eye(t + 1)
+    o, lse = ref(q, k, eye[1:][None, None], k_hat[0][None, None], eye[0][None, None], rows=[t - 1])
+    a = k_hat[: t + 1] @ q_t
+    return np.log(o[0, 0, 0]) + lse[0, 0, 0] - a, a
+
+
+def dev_taylor_b(ref, eps, seed=3, t=6):
+    """|b - second-order Taylor| for logits of size eps (should scale as eps^3).
+
+    Interior: b = (L + R)/6 + (L^2 - L R + R^2)/36 + O(3), L = a_{i-1} - a_i,
+    R = a_{i+1} - a_i (first order: eq. (13)).  Ends: b = -ln 2 + x/3 + x^2/36
+    + O(3) with x the single neighbour difference.
+    """
+    rng = np.random.default_rng(seed)
+    d = 4
+    q_t = rng.standard_normal(d) * eps
+    k_hat = rng.standard_normal((t + 1, d))
+    b, a = implied_b(ref, q_t, k_hat, t)
+    worst = 0.0
+    for i in range(t + 1):
+        if i == 0 or i == t:
+            x = a[1] - a[0] if i == 0 else a[t - 1] - a[t]
+            approx = -math.log(2.0) + x / 3 + x * x / 36
+        else:
+            L, R = a[i - 1] - a[i], a[i + 1] - a[i]
+            approx = (L + R) / 6 + (L * L - L * R + R * R) / 36
+        worst = max(worst, abs(b[i] - approx))
+    return worst
+
+
+def dev_copied_sink(ref, seed=4):
+    """k_0 = k_1, v_0 = v_1: the first segment is flat, so o_1 = v_1, lse_1 = a_1."""
+    q, k, v, _, _ = random_case(seed)
+    k0, v0 = k[:, :, 0].copy(), v[:, :, 0].copy()
+    o, lse = ref(q, k, v, k0, v0, rows=[0])
+    a1 = float(q[0, 0, 0] @ k[0, 0, 0])
+    return max(float(np.abs(o[0, 0, 0] - v[0, 0, 0]).max()), abs(float(lse[0, 0, 0]) - a1))

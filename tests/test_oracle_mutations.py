@@ -1,0 +1,62 @@
+"""Plant plausible mistakes in a copy of the CPU reference and show the pins catch each.
+
+The reference's source text is edited in memory (never on disk), executed as a
+throw-away module, and run through the checks of ``pins``.  A mutant passes
+only if every check stays within its tolerance -- which must never happen.
+"""
+
+import inspect
+
+import pytest
+
+import oracle.csa as oracle_csa
+import pins
+
+MUTATIONS = {
+    "sign of delta": ("delta = a[1:] - a_left", "delta = a_left - a[1:]"),
+    "sign of the phi_2 term": ("(v_im1 - v_i))", "(v_i - v_im1))"),
+    "dropped phi_2 term": ("f1[:, None] * v_i + f2[:, None] * (v_im1 - v_i)", "f1[:, None] * v_i"),
+    "phi_2 in the denominator": ("seg_den = e_left * f1", "seg_den = e_left * f2"),
+    "value index shifted": ("v_i = V[1:]", "v_i = V[:-1]"),
+    "exponent on the right end": ("e_left = np.exp(a_left - shift)", "e_left = np.exp(a[1:] - shift)"),
+    "phi_2 series coefficients": ("math.factorial(n + 2)", "math.factorial(n + 1)"),
+    "phi_2 closed form sign": ("(np.expm1(safe) - safe)", "(np.expm1(safe) + safe)"),
+    "lse without the shift": ("lse = shift + math.log(den)", "lse = math.log(den)"),
+    "position 0 dropped": ("K = k_hat[: t + 1]", "K = np.concatenate([k_hat[1:2], k_hat[1 : t + 1]])"),
+    "value at position 0 dropped": ("V = v_hat[: t + 1]",
+                                    "V = np.concatenate([0 * v_hat[:1], v_hat[1 : t + 1]])"),
+}
+
+CHECKS = [
+    (pins.dev_vs_quadrature, 1e-12),
+    (pins.dev_trapezoid, 1e-13),
+    (pins.dev_linear_ramp, 1e-11),
+    (pins.dev_vs_simplified, 1e-12),
+    (pins.dev_copied_sink, 1e-13),
+    (lambda ref: pins.dev_vs_quadrature(ref, seed=6, scale=0.05), 1e-12),
+]
+
+
+def _mutant(old, new):
+    src = inspect.getsource(oracle_csa)
+    assert src.count(old) == 1, f"mutation anchor not unique: {old!r}"
+    ns = {"__name__": "oracle_mutant"}
+    exec(compile(src.replace(old, new), "<oracle mutant>", "exec"), ns)
+    return ns["csa_reference"]
+
+
+def test_unmutated_reference_passes_every_check():
+    for check, tol in CHECKS:
+        assert check(oracle_csa.csa_reference) < tol
+
+
+@pytest.mark.parametrize("name", sorted(MUTATIONS))
+def test_mutant_is_caught(name):
+    ref = _mutant(*MUTATIONS[name])
+    caught = []
+    for check, tol in CHECKS:
+        try:
+            caught.append(not (check(ref) < tol))
+        except Exception:
+            caught.append(True)
+    assert any(caught), f"mutation '{name}' escaped every pin"

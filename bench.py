@@ -1,0 +1,206 @@
+"""Throughput of the causal continuous-softmax-attention forward on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload lm] [--no-cpu-baseline]
+
+One step = one csa_forward call over the whole workload (every query row of
+every batch and head); inputs are resident in HBM before the timed region.
+Metric: TFLOP/s counting 4 T^2 d / 2 FLOP per (batch, head) -- QK^T plus PV
+over the causal half, the convention under which the pages call continuous
+and standard attention "essentially the same" in FLOPs -- and the fraction of
+the MI355X dense bf16 MFMA peak.  The standard-attention kernel built on the
+same tiling (std_fwd) runs on the same inputs for the ratio.
+
+Prints ONE JSON line.  `cpu_baseline` times the float64 CPU reference on a
+bounded sample of query rows of the same workload (process pool over host
+cores), scaled to TFLOP/s by the same FLOP convention.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, published
+PEAK_F32_TFLOPS = 157.3     # MI355X dense fp32 MFMA, published
+PEAK_HBM_GBS = 8000.0
+
+METRIC = "continuous-attn fwd TFLOP/s + % bf16 MFMA peak, B4 H16 T4096 d128"
+
+
+# ------------------------------------------------------------------ CPU leg
+
+_CPU = {}
+
+
+def _cpu_task(args):
+    import numpy as np
+
+    from oracle import csa_reference
+
+    b, h, rows = args
+    q, k, v = _CPU["q"], _CPU["k"], _CPU["v"]
+    sl = (slice(b, b + 1), slice(h, h + 1))
+    csa_reference(q[sl], k[sl], v[sl], None if _CPU["k0"] is None else _CPU["k0"][sl],
+                  None if _CPU["v0"] is None else _CPU["v0"][sl], rows=rows)
+    return int(np.sum(rows + 1))
+
+
+def cpu_baseline(w, q, k, v, k0, v0, heads=64, rows_per_head=32, seed=123):
+    """Time the float64 reference on a seeded sample of (head, row) pairs.
+
+    Runs before any GPU work (the pool forks).  Returns the cpu_baseline object.
+    """
+    import multiprocessing as mp
+
+    import numpy as np
+
+    rng = np.random.default_rng(seed)
+    nheads = w.B * w.H
+    pick = rng.choice(nheads, size=min(heads, nheads), replace=False)
+    tasks = []
+    for bh in pick:
+        rows = np.sort(rng.choice(w.T, size=rows_per_head, replace=False))
+        tasks.append((int(bh) // w.H, int(bh) % w.H, rows))
+    _CPU.update(q=q.float().numpy(), k=k.float().numpy(), v=v.float().numpy(),
+                k0=None if k0 is None else k0.float().numpy(), v0=None if v0 is None else v0.float().numpy())
+    workers = max(1, min(16, len(os.sched_getaffinity(0))))
+    os.environ.setdefault("OMP_NUM_THREADS", "1")
+    ctx = mp.get_context("fork")
+    t0 = time.perf_counter()
+    with ctx.Pool(workers) as pool:
+        done = pool.map(_cpu_task, tasks, chunksize=1)
+    dt = time.perf_counter() - t0
+    positions = sum(done)                      # sum over sampled rows of (t + 1)
+    flop = 4.0 * w.d * positions               # same convention as the metric
+    total_rows = w.B * w.H * w.T
+    return {
+        "value": flop / dt / 1e12,
+        "unit": "TFLOP/s",
+        "cores": workers,
+        "kind": "oracle",
+        "sample": (f"{len(tasks)} of {nheads} heads x {rows_per_head} seeded query rows "
+                   f"({len(tasks) * rows_per_head} of {total_rows} rows), float64 eq. (8), "
+                   f"{workers} worker processes, {dt:.1f} s wall"),
+    }
+
+
+# ------------------------------------------------------------------ GPU leg
+
+def time_kernel(fn, steps, warmup, stream):
+    """Average per-launch duration (ms) from HIP events on the launch stream, and
+    the wall time (ms) of the whole timed region bracketed by synchronisations."""
+    import torch
+
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        starts[i].record(stream)
+        fn()
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t0) * 1e3
+    per = [s.elapsed_time(e) for s, e in zip(starts, ends)]
+    return sum(per) / len(per), min(per), wall_ms
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="lm")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-std", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: there is no multi-GPU path "
+              "(independent (batch, head) shards need no communication); run with --gpus 1",
+              file=sys.stderr)
+        sys.exit(2)
+
+    from workloads import WORKLOADS, make_inputs
+
+    w = WORKLOADS[args.workload]
+    q, k, v, k0, v0 = make_inputs(w)
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(w, q, k, v, k0, v0)
+
+    import torch
+
+    import continuous_softmax_attention_amd as csa
+
+    dev = torch.device("cuda:0")
+    qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
+    k0d = None if k0 is None else k0.to(dev)
+    v0d = None if v0 is None else v0.to(dev)
+    out = torch.empty_like(qd)
+    lse = torch.empty((w.B, w.H, w.T), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step():
+        csa.csa_forward(qd, kd, vd, k0d, v0d, out=out, lse=lse, stream=stream)
+
+    avg_ms, min_ms, wall_ms = time_kernel(step, args.steps, args.warmup, stream)
+    flop = float(w.flop)
+    tflops = flop / (avg_ms * 1e-3) / 1e12
+    peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_TFLOPS
+
+    res = {
+        "metric": METRIC,
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall_ms / args.steps, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {"workload": f"{w.name}: causal CSA forward B{w.B} H{w.H} T{w.T} d{w.d} {w.dtype}"
+                               + (", RoPE on q,k" if w.rope else "") + f", k0/v0 {w.sink}",
+                   "B": w.B, "H": w.H, "T": w.T, "d": w.d},
+        "pct_peak": round(100.0 * tflops / peak, 2),
+        "kernel_ms": {"avg": round(avg_ms, 4), "min": round(min_ms, 4)},
+        "roofline": {
+            "bound": "mfma",
+            "achieved": round(tflops, 2),
+            "peak": peak,
+            "unit": "TFLOP/s",
+            "frac": round(tflops / peak, 4),
+            "traffic": None,
+        },
+    }
+    if not args.no_std:
+        sout = torch.empty_like(qd)
+        slse = torch.empty_like(lse)
+
+        def std_step():
+            csa.std_fwd(qd, kd, vd, out=sout, lse=slse, stream=stream)
+
+        s_avg, _, _ = time_kernel(std_step, args.steps, args.warmup, stream)
+        s_tflops = flop / (s_avg * 1e-3) / 1e12
+        res["std_attention"] = {"value": round(s_tflops, 2), "unit": "TFLOP/s", "kernel_ms": round(s_avg, 4),
+                                "pct_peak": round(100.0 * s_tflops / peak, 2)}
+        res["ratio_vs_std"] = round(tflops / s_tflops, 4)
+    if cpu is not None:
+        res["cpu_baseline"] = cpu
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,31 @@
+"""Causal continuous softmax attention forward for AMD MI355X (gfx950).
+
+The compute path is the C-ABI library ``libcsa.so`` (hand-written HIP
+kernels, include/csa.h); this package only marshals arguments to it.
+``std_fwd`` (``libcsa_bench.so``) is standard softmax attention on the same
+tiling, kept as a throughput comparison point.
+
+Method: J. Su, "Continuous Softmax Attention" -- keys and values linearly
+interpolated between positions with an extra k_0, v_0 (eq. (2)-(3)), reduced
+to softmax attention with a neighbour-dependent correction (eq. (10)-(11)).
+"""
+
+from ._lib import (  # noqa: F401
+    CSA_BF16,
+    CSA_ERR_HIP,
+    CSA_ERR_INVALID_ARG,
+    CSA_ERR_UNSUPPORTED,
+    CSA_F32,
+    CSA_OK,
+    CsaError,
+    csa_forward,
+    csa_forward_check,
+    csa_forward_raw,
+    header_functions,
+    library_path,
+    load,
+    status_string,
+    std_fwd,
+    std_fwd_check,
+    std_fwd_raw,
+)

@@ -1,0 +1,196 @@
+"""ctypes binding of the C-ABI in include/csa.h and include/csa_bench.h.
+
+Argument marshalling only: tensors are checked and turned into device
+pointers, the call runs on the caller's (or torch's current) HIP stream, and
+a non-zero status becomes a ``CsaError``.  All arithmetic happens in the HIP
+kernels; if the libraries are missing the calls raise instead of falling back
+to anything else.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+INCLUDE = os.path.join(os.path.dirname(PKG), "include")
+
+CSA_F32 = 0
+CSA_BF16 = 1
+CSA_OK = 0
+CSA_ERR_INVALID_ARG = 1
+CSA_ERR_UNSUPPORTED = 2
+CSA_ERR_HIP = 3
+
+
+class CsaError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what} failed with status {status}: {status_string(status)}")
+
+
+_vp = ctypes.c_void_p
+_i64 = ctypes.c_int64
+_SIGS = {
+    "csa_forward": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, ctypes.c_int, _vp]),
+    "csa_forward_check": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, ctypes.c_int]),
+    "csa_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    "std_fwd": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, ctypes.c_int, _vp]),
+    "std_fwd_check": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, ctypes.c_int]),
+}
+
+_handles: dict[str, ctypes.CDLL] = {}
+
+
+def library_path(name: str = "libcsa.so") -> str:
+    return os.path.join(PKG, name)
+
+
+def load(name: str = "libcsa.so") -> ctypes.CDLL:
+    """Load an in-tree library (built by ``continuous_softmax_attention_amd.build``)."""
+    if name in _handles:
+        return _handles[name]
+    path = library_path(name)
+    if not os.path.exists(path):
+        raise RuntimeError(
+            f"{path} is not built; run `python -m continuous_softmax_attention_amd.build` "
+            "(the HIP path has no fallback)")
+    lib = ctypes.CDLL(path)
+    for sym, (res, args) in _SIGS.items():
+        if hasattr(lib, sym):
+            fn = getattr(lib, sym)
+            fn.restype = res
+            fn.argtypes = args
+    _handles[name] = lib
+    return lib
+
+
+def header_functions(header: str) -> list[str]:
+    """Names of the functions a public header declares."""
+    with open(os.path.join(INCLUDE, header)) as f:
+        text = f.read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(", text, flags=re.M)
+
+
+def status_string(status: int) -> str:
+    try:
+        return load().csa_status_string(int(status)).decode()
+    except Exception:  # library missing: still give a readable message
+        return {0: "ok", 1: "invalid argument", 2: "unsupported", 3: "HIP launch failure"}.get(status, "unknown")
+
+
+# ---------------------------------------------------------------- raw pointers
+
+def csa_forward_raw(q, k, v, k0, v0, out, lse, B, H, T, d, dtype, stream=0) -> int:
+    """Direct C-ABI call with integer device pointers; returns the status code."""
+    return load().csa_forward(q, k, v, k0 or None, v0 or None, out, lse or None, B, H, T, d, dtype, stream or None)
+
+
+def std_fwd_raw(q, k, v, out, lse, B, H, T, d, dtype, stream=0) -> int:
+    return load("libcsa_bench.so").std_fwd(q, k, v, out, lse or None, B, H, T, d, dtype, stream or None)
+
+
+def csa_forward_check(q, k, v, k0, v0, out, lse, B, H, T, d, dtype) -> int:
+    return load().csa_forward_check(q, k, v, k0, v0, out, lse, B, H, T, d, dtype)
+
+
+def std_fwd_check(q, k, v, out, lse, B, H, T, d, dtype) -> int:
+    return load("libcsa_bench.so").std_fwd_check(q, k, v, out, lse, B, H, T, d, dtype)
+
+
+# ---------------------------------------------------------------- torch tensors
+
+def _dtype_code(t):
+    import torch
+
+    if t.dtype == torch.float32:
+        return CSA_F32
+    if t.dtype == torch.bfloat16:
+        return CSA_BF16
+    raise TypeError(f"unsupported dtype {t.dtype}; expected float32 or bfloat16")
+
+
+def _check(name, t, shape, dtype, device):
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _stream_handle(stream, device):
+    import torch
+
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def csa_forward(q, k, v, k0=None, v0=None, *, out=None, lse=None, return_lse=True, stream=None):
+    """Continuous softmax attention forward (causal) through libcsa.
+
+    q, k, v: [B, H, T, d] float32 or bfloat16 device tensors (same dtype);
+    k0, v0: [B, H, d] or None (zeros).  Returns (out, lse) -- lse is float32
+    [B, H, T] (None when return_lse is False and no lse buffer is given).
+    """
+    import torch
+
+    if q.dim() != 4:
+        raise ValueError("q must be [B, H, T, d]")
+    B, H, T, d = q.shape
+    dt = q.dtype
+    dev = q.device
+    if dev.type != "cuda":
+        raise ValueError("csa_forward runs on the GPU only; inputs must be device tensors")
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _check(name, t, (B, H, T, d), dt, dev)
+    for name, t in (("k0", k0), ("v0", v0)):
+        if t is not None:
+            _check(name, t, (B, H, d), dt, dev)
+    if out is None:
+        out = torch.empty_like(q)
+    else:
+        _check("out", out, (B, H, T, d), dt, dev)
+    if lse is None and return_lse:
+        lse = torch.empty((B, H, T), dtype=torch.float32, device=dev)
+    elif lse is not None:
+        _check("lse", lse, (B, H, T), torch.float32, dev)
+    st = load().csa_forward(
+        q.data_ptr(), k.data_ptr(), v.data_ptr(),
+        k0.data_ptr() if k0 is not None else None, v0.data_ptr() if v0 is not None else None,
+        out.data_ptr(), lse.data_ptr() if lse is not None else None,
+        B, H, T, d, _dtype_code(q), _stream_handle(stream, dev))
+    if st != CSA_OK:
+        raise CsaError(st, "csa_forward")
+    return out, lse
+
+
+def std_fwd(q, k, v, *, out=None, lse=None, return_lse=True, stream=None):
+    """Standard causal softmax attention (the comparator) through libcsa_bench."""
+    import torch
+
+    B, H, T, d = q.shape
+    dt, dev = q.dtype, q.device
+    if dev.type != "cuda":
+        raise ValueError("std_fwd runs on the GPU only; inputs must be device tensors")
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _check(name, t, (B, H, T, d), dt, dev)
+    if out is None:
+        out = torch.empty_like(q)
+    else:
+        _check("out", out, (B, H, T, d), dt, dev)
+    if lse is None and return_lse:
+        lse = torch.empty((B, H, T), dtype=torch.float32, device=dev)
+    elif lse is not None:
+        _check("lse", lse, (B, H, T), torch.float32, dev)
+    st = load("libcsa_bench.so").std_fwd(
+        q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+        lse.data_ptr() if lse is not None else None, B, H, T, d, _dtype_code(q), _stream_handle(stream, dev))
+    if st != CSA_OK:
+        raise CsaError(st, "std_fwd")
+    return out, lse

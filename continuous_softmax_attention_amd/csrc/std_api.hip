@@ -1,0 +1,31 @@
+// C-ABI entry points of libcsa_bench: standard causal attention on the CSA tiling.
+#include <hip/hip_runtime.h>
+
+#include "attn_fwd.hpp"
+#include "csa_bench.h"
+#include "validate.hpp"
+
+extern "C" int std_fwd_check(const void* q, const void* k, const void* v, const void* out,
+                             const float* lse, int64_t B, int64_t H, int64_t T, int64_t d,
+                             int dtype) {
+  return csa::validate(q, k, v, nullptr, nullptr, out, lse, B, H, T, d, dtype, false);
+}
+
+extern "C" int std_fwd(const void* q, const void* k, const void* v, void* out, float* lse,
+                       int64_t B, int64_t H, int64_t T, int64_t d, int dtype, void* stream) {
+  const int st = csa::validate(q, k, v, nullptr, nullptr, out, lse, B, H, T, d, dtype, false);
+  if (st != CSA_OK) return st;
+  csa::FwdParams p{q, k, v, nullptr, nullptr, out, lse, (int)B, (int)H, (int)T, 0};
+  hipError_t e = hipErrorInvalidValue;
+  hipStream_t s = (hipStream_t)stream;
+  if (dtype == CSA_F32) {
+    if (d == 16) e = csa::launch_attn<float, 16, false>(p, s);
+    else if (d == 64) e = csa::launch_attn<float, 64, false>(p, s);
+    else e = csa::launch_attn<float, 128, false>(p, s);
+  } else {
+    if (d == 16) e = csa::launch_attn<csa::bf16, 16, false>(p, s);
+    else if (d == 64) e = csa::launch_attn<csa::bf16, 64, false>(p, s);
+    else e = csa::launch_attn<csa::bf16, 128, false>(p, s);
+  }
+  return e == hipSuccess ? CSA_OK : CSA_ERR_HIP;
+}

@@ -1,0 +1,73 @@
+// Host-side argument validation shared by csa_forward and std_fwd.
+// Pure C++: no HIP call, no memory access.
+#pragma once
+
+#include <cstdint>
+
+#include "csa.h"
+
+namespace csa {
+
+struct Span {
+  uintptr_t lo = 0, hi = 0;  // [lo, hi)
+  bool valid() const { return hi > lo; }
+};
+
+inline bool overlaps(Span a, Span b) { return a.valid() && b.valid() && a.lo < b.hi && b.lo < a.hi; }
+
+inline Span span_of(const void* p, int64_t bytes) {
+  Span s;
+  if (p) {
+    s.lo = reinterpret_cast<uintptr_t>(p);
+    s.hi = s.lo + static_cast<uintptr_t>(bytes);
+  }
+  return s;
+}
+
+inline bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+// Checks shared by both entry points.  `with_sink` adds the k0/v0 buffers.
+inline int validate(const void* q, const void* k, const void* v, const void* k0, const void* v0,
+                    const void* out, const float* lse, int64_t B, int64_t H, int64_t T, int64_t d,
+                    int dtype, bool with_sink) {
+  if (dtype != CSA_F32 && dtype != CSA_BF16) return CSA_ERR_UNSUPPORTED;
+  if (d != 16 && d != 64 && d != 128) return CSA_ERR_UNSUPPORTED;
+  if (!q || !k || !v || !out) return CSA_ERR_INVALID_ARG;
+  if (B < 1 || H < 1 || T < 1) return CSA_ERR_INVALID_ARG;
+  // size limits: grid of ceil(T/128) * B * H work-groups; 32-bit row indices
+  const int64_t kMax32 = (int64_t(1) << 31) - 1;
+  if (T > kMax32 / 2 || B > kMax32 || H > kMax32) return CSA_ERR_INVALID_ARG;
+  if (B * H > kMax32 / ((T + 127) / 128)) return CSA_ERR_INVALID_ARG;
+  const int64_t esize = dtype == CSA_F32 ? 4 : 2;
+  if (B * H > INT64_MAX / (T * d * esize)) return CSA_ERR_INVALID_ARG;
+  for (const void* p : {q, k, v, out})
+    if (!aligned(p, 16)) return CSA_ERR_INVALID_ARG;
+  if (with_sink) {
+    if (k0 && !aligned(k0, 16)) return CSA_ERR_INVALID_ARG;
+    if (v0 && !aligned(v0, 16)) return CSA_ERR_INVALID_ARG;
+  }
+  if (lse && !aligned(lse, 4)) return CSA_ERR_INVALID_ARG;
+  const int64_t big = B * H * T * d * esize;
+  const Span so = span_of(out, big), sl = span_of(lse, B * H * T * 4);
+  Span ins[5] = {span_of(q, big), span_of(k, big), span_of(v, big), {}, {}};
+  if (with_sink) {
+    ins[3] = span_of(k0, B * H * d * esize);
+    ins[4] = span_of(v0, B * H * d * esize);
+  }
+  for (const Span& s : ins)
+    if (overlaps(so, s) || overlaps(sl, s)) return CSA_ERR_INVALID_ARG;
+  if (overlaps(so, sl)) return CSA_ERR_INVALID_ARG;
+  return CSA_OK;
+}
+
+inline const char* status_string(int s) {
+  switch (s) {
+    case CSA_OK: return "ok";
+    case CSA_ERR_INVALID_ARG: return "invalid argument (null pointer, size, alignment or overlap)";
+    case CSA_ERR_UNSUPPORTED: return "unsupported head dimension or dtype";
+    case CSA_ERR_HIP: return "HIP launch failure";
+    default: return "unknown status";
+  }
+}
+
+}  // namespace csa

@@ -1,0 +1,96 @@
+/*
+ * libcsa -- causal forward pass of continuous softmax attention on AMD
+ * Instinct MI355X (gfx950).
+ *
+ * Method: J. Su, "Continuous Softmax Attention" (Scientific Spaces; English
+ * translation on tylerromero.com).  Keys and values are linearly interpolated
+ * between integer positions (Problem Statement, eq. (3)), with two extra
+ * vectors k_0, v_0 at position 0, and the attention sum of standard softmax
+ * attention becomes the ratio of two integrals over [0, t] (eq. (2)).  The
+ * integrals reduce (Assembly and Simplification, eq. (10)-(11)) to
+ *
+ *     o_t = sum_{i=0..t} e^{a_{t,i} + b_{t,i}} v_i / sum_{i=0..t} e^{a_{t,i} + b_{t,i}},
+ *     a_{t,i} = q_t . k_i,
+ *     e^{b_{t,i}} = phi_2(a_{t,i-1} - a_{t,i}) + phi_2(a_{t,i+1} - a_{t,i}),
+ *
+ * where only the existing neighbour enters at i = 0 and i = t, and
+ * phi_2(x) = (e^x - 1 - x)/x^2, phi_2(0) = 1/2 (Preliminaries, eq. (6)).
+ *
+ * Conventions shared by every entry point:
+ *   - Query t = 1..T is row t-1 of q; key/value position i >= 1 is row i-1
+ *     of k/v; position 0 is k0/v0.  No 1/sqrt(d) scale is applied inside:
+ *     the logit is the bare dot product q_t . k_i, as in eq. (1)-(2).
+ *   - All device buffers are owned by the caller; the library allocates no
+ *     memory and keeps no state between calls (thread-safe, re-entrant).
+ *   - Calls are asynchronous on `stream` (a hipStream_t; NULL = the null
+ *     stream) and do not synchronise.  Device-side faults surface through
+ *     the HIP runtime of the caller, not through the return value.
+ *   - Every argument is validated before any HIP API call; on failure the
+ *     call returns an error code and launches nothing.
+ */
+#ifndef LIBCSA_CSA_H
+#define LIBCSA_CSA_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Element types of q, k, v, k0, v0 and out. */
+typedef enum {
+  CSA_F32 = 0,  /* IEEE float32 */
+  CSA_BF16 = 1  /* bfloat16 (round-to-nearest-even on output) */
+} csa_dtype;
+
+/* Return codes. */
+enum {
+  CSA_OK = 0,
+  CSA_ERR_INVALID_ARG = 1, /* NULL pointer, non-positive size, misaligned or overlapping buffer, size overflow */
+  CSA_ERR_UNSUPPORTED = 2, /* head dimension d not in {16, 64, 128}, or unknown dtype */
+  CSA_ERR_HIP = 3          /* the kernel launch was rejected by the HIP runtime */
+};
+
+/*
+ * csa_forward -- o_t and lse_t for every query t = 1..T of every (batch, head)
+ * by eq. (10)-(11) of "Continuous Softmax Attention" (the causal interval
+ * [0, t] chosen under Problem Statement).
+ *
+ *   q, k, v  device, [B, H, T, d] contiguous, element type `dtype`, 16-byte aligned.
+ *   k0, v0   device, [B, H, d] contiguous, `dtype`, 16-byte aligned; NULL means
+ *            a zero vector (the "all zeros" choice under Analysis of the
+ *            Result).  For the "copy the first key" choice pass a copy of
+ *            k[:, :, 0, :] (resp. v).
+ *   out      device, [B, H, T, d] contiguous, `dtype`, 16-byte aligned; must not
+ *            overlap any input or lse.  Accumulation is float32; bf16 output is
+ *            rounded to nearest even.
+ *   lse      device, [B, H, T] float32, 4-byte aligned, or NULL (not written):
+ *            natural log of sum_i e^{a_{t,i} + b_{t,i}}, i.e. of the
+ *            denominator integral of eq. (2).
+ *   B, H, T  >= 1.  d in {16, 64, 128}.
+ *   dtype    CSA_F32 or CSA_BF16.
+ *   stream   hipStream_t or NULL.
+ *
+ * Returns CSA_OK, or an error code from the enum above (nothing launched).
+ */
+int csa_forward(const void* q, const void* k, const void* v, const void* k0, const void* v0,
+                void* out, float* lse, int64_t B, int64_t H, int64_t T, int64_t d, int dtype,
+                void* stream);
+
+/*
+ * csa_forward_check -- the argument validation of csa_forward alone, with
+ * the same arguments and the same return codes; touches no memory and makes
+ * no HIP call (usable on a machine without a GPU).
+ */
+int csa_forward_check(const void* q, const void* k, const void* v, const void* k0, const void* v0,
+                      const void* out, const float* lse, int64_t B, int64_t H, int64_t T, int64_t d,
+                      int dtype);
+
+/* Static, NUL-terminated description of a return code. */
+const char* csa_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LIBCSA_CSA_H */

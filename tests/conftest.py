@@ -16,7 +16,7 @@ def pytest_configure(config):
 
 
 def pytest_collection_modifyitems(config, items):
-    """GPU tests skip on a machine without a GPU; on a GPU machine they run and fail loudly."""
+    """GPU tests skip on a machine without a GPU; where a GPU is present they run and fail loudly."""
     try:
         import torch
 

@@ -1,0 +1,131 @@
+"""The C-ABI boundary on the CPU: the libraries load, export every declared
+symbol, and validate arguments before touching the GPU.
+
+No kernel is launched here: ``*_check`` entry points run the validation alone,
+and every ``csa_forward`` call below is made with arguments the validation
+rejects, so it returns before any HIP call.
+"""
+
+import ctypes
+import os
+
+import pytest
+
+import continuous_softmax_attention_amd as csa
+from continuous_softmax_attention_amd import build as csa_build
+
+OK, INV, UNS = csa.CSA_OK, csa.CSA_ERR_INVALID_ARG, csa.CSA_ERR_UNSUPPORTED
+
+
+@pytest.fixture(scope="module", autouse=True)
+def built():
+    missing = [n for n in csa_build.LIBS if not os.path.exists(csa.library_path(n))]
+    if missing:  # the libraries cross-compile on a machine without a GPU
+        csa_build.build()
+
+
+@pytest.mark.parametrize("lib,header", [("libcsa.so", "csa.h"), ("libcsa_bench.so", "csa_bench.h")])
+def test_exports_every_declared_symbol(lib, header):
+    names = csa.header_functions(header)
+    assert names, header
+    handle = ctypes.CDLL(csa.library_path(lib))
+    for n in names:
+        assert hasattr(handle, n), f"{lib} does not export {n} declared in {header}"
+
+
+def test_header_declares_the_entry_points():
+    assert {"csa_forward", "csa_forward_check", "csa_status_string"} <= set(csa.header_functions("csa.h"))
+    assert {"std_fwd", "std_fwd_check"} <= set(csa.header_functions("csa_bench.h"))
+
+
+A = 0x10000  # fake, 16-byte-aligned addresses: validation never dereferences them
+MB = 1 << 20
+
+
+def _args(**kw):
+    a = dict(q=A, k=A + 64 * MB, v=A + 128 * MB, k0=None, v0=None, out=A + 192 * MB, lse=A + 256 * MB,
+             B=2, H=3, T=100, d=64, dtype=csa.CSA_BF16)
+    a.update(kw)
+    return a
+
+
+def _check(**kw):
+    a = _args(**kw)
+    return csa.csa_forward_check(a["q"], a["k"], a["v"], a["k0"], a["v0"], a["out"], a["lse"],
+                                 a["B"], a["H"], a["T"], a["d"], a["dtype"])
+
+
+def test_valid_arguments_pass():
+    assert _check() == OK
+    assert _check(k0=A + 300 * MB, v0=A + 301 * MB) == OK
+    assert _check(lse=None) == OK
+    for d in (16, 64, 128):
+        for dt in (csa.CSA_F32, csa.CSA_BF16):
+            assert _check(d=d, dtype=dt) == OK
+    assert _check(T=1, B=1, H=1) == OK
+
+
+@pytest.mark.parametrize("field", ["q", "k", "v", "out"])
+def test_null_required_pointer(field):
+    assert _check(**{field: None}) == INV
+
+
+@pytest.mark.parametrize("d", [0, 1, 8, 32, 96, 256])
+def test_unsupported_head_dim(d):
+    assert _check(d=d) == UNS
+
+
+@pytest.mark.parametrize("dt", [-1, 2, 7])
+def test_unsupported_dtype(dt):
+    assert _check(dtype=dt) == UNS
+
+
+@pytest.mark.parametrize("kw", [dict(B=0), dict(H=0), dict(T=0), dict(T=-5), dict(B=-1)])
+def test_non_positive_sizes(kw):
+    assert _check(**kw) == INV
+
+
+@pytest.mark.parametrize("field,off", [("q", 8), ("k", 4), ("v", 2), ("out", 8), ("k0", 8), ("v0", 4), ("lse", 2)])
+def test_misaligned(field, off):
+    base = _args(k0=A + 300 * MB, v0=A + 301 * MB)
+    assert _check(**{**base, field: base[field] + off}) == INV
+
+
+def test_overlapping_output():
+    assert _check(out=A + 64 * MB + 4096) == INV            # out inside k
+    assert _check(lse=A + 1024) == INV                      # lse inside q
+    assert _check(lse=A + 192 * MB + 16) == INV             # lse inside out
+    assert _check(k0=A + 300 * MB, out=A + 300 * MB - 16) == INV  # out runs into k0
+
+
+def test_size_overflow_rejected():
+    assert _check(B=1 << 31) == INV
+    assert _check(T=1 << 40) == INV
+
+
+def test_forward_rejects_before_any_hip_call():
+    # an invalid call must return its code without touching the (absent) GPU
+    assert csa.csa_forward_raw(None, A, A, None, None, A + MB, None, 1, 1, 8, 64, csa.CSA_F32) == INV
+    assert csa.csa_forward_raw(A, A + MB, A + 2 * MB, None, None, A + 3 * MB, None, 1, 1, 8, 48, csa.CSA_F32) == UNS
+    assert csa.std_fwd_raw(A, A + MB, A + 2 * MB, A + 3 * MB, None, 1, 1, 0, 64, csa.CSA_F32) == INV
+
+
+def test_std_check_matches_rules():
+    assert csa.std_fwd_check(A, A + MB, A + 2 * MB, A + 3 * MB, None, 1, 2, 64, 128, csa.CSA_BF16) == OK
+    assert csa.std_fwd_check(A, A + MB, A + 2 * MB, A + MB, None, 1, 2, 64, 128, csa.CSA_BF16) == INV
+    assert csa.std_fwd_check(A, A + MB, A + 2 * MB, A + 3 * MB, None, 1, 2, 64, 100, csa.CSA_BF16) == UNS
+
+
+def test_status_strings():
+    for s in (OK, INV, UNS, csa.CSA_ERR_HIP, 99):
+        assert isinstance(csa.status_string(s), str) and csa.status_string(s)
+
+
+def test_python_binding_refuses_cpu_tensors():
+    import torch
+
+    q = torch.zeros(1, 1, 4, 16)
+    with pytest.raises(ValueError):
+        csa.csa_forward(q, q, q)
+    with pytest.raises(ValueError):
+        csa.std_fwd(q, q, q)

@@ -91,12 +91,10 @@ def rope_interleaved(x: torch.Tensor, base: float = 10000.0) -> torch.Tensor:
     ang = torch.arange(T, dtype=torch.float64)[:, None] * inv[None, :]
     cos = torch.cos(ang).to(torch.float32)
     sin = torch.sin(ang).to(torch.float32)
-    x0 = x[..., 0::2]
-    x1 = x[..., 1::2]
-    out = torch.empty_like(x)
-    out[..., 0::2] = x0 * cos - x1 * sin
-    out[..., 1::2] = x0 * sin + x1 * cos
-    return out
+    pairs = x.reshape(B, H, T, d // 2, 2)
+    x0 = pairs[..., 0]
+    x1 = pairs[..., 1]
+    return torch.stack((x0 * cos - x1 * sin, x0 * sin + x1 * cos), dim=-1).reshape(B, H, T, d)
 
 
 def make_inputs(w: Workload | str, *, B=None, H=None, T=None, d=None, dtype=None, seed=None):

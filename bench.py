@@ -115,6 +115,29 @@ def time_kernel(fn, steps, warmup, stream):
     return sum(per) / len(per), min(per), wall_ms
 
 
+def counters_mode(w, q, k, v, k0, v0):
+    """One launch of each kernel plus a 256 MiB device-to-device copy whose HBM bytes
+    are known (256 MiB read + 256 MiB written), to scale FETCH_SIZE/WRITE_SIZE."""
+    import torch
+
+    import continuous_softmax_attention_amd as csa
+
+    dev = torch.device("cuda:0")
+    src = torch.ones(1 << 26, dtype=torch.float32, device=dev)   # 256 MiB
+    dst = torch.empty_like(src)
+    qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
+    k0d = None if k0 is None else k0.to(dev)
+    v0d = None if v0 is None else v0.to(dev)
+    torch.cuda.synchronize()
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    csa.csa_forward(qd, kd, vd, k0d, v0d)
+    torch.cuda.synchronize()
+    csa.std_fwd(qd, kd, vd)
+    torch.cuda.synchronize()
+    print(json.dumps({"counters_run": w.name, "copy_bytes": 2 * src.numel() * 4}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -123,6 +146,9 @@ def main():
     ap.add_argument("--workload", default="lm")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-std", action="store_true")
+    ap.add_argument("--counters", action="store_true",
+                    help="for rocprofv3 --pmc passes: one plain device copy of 256 MiB (counter "
+                         "calibration), one csa_forward and one std_fwd launch, then exit")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: there is no multi-GPU path "
@@ -134,6 +160,8 @@ def main():
 
     w = WORKLOADS[args.workload]
     q, k, v, k0, v0 = make_inputs(w)
+    if args.counters:
+        return counters_mode(w, q, k, v, k0, v0)
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(w, q, k, v, k0, v0)

@@ -51,6 +51,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
+#include <type_traits>
 
 namespace csa {
 
@@ -195,16 +196,28 @@ __device__ __forceinline__ void edge_terms(float al, float pl, float ar, float p
   edge<F32>(al, pl, ar, pr, 0.0f, R, L);
 }
 
+// Rescale the bf16 row sums: lanes 0..15 hold queries n' (element 0) and n' + 16
+// (element 1) of the 16x16x32 accumulator; the second takes the factor of lane n' + 16.
+__device__ __forceinline__ void rescale_lacc(f32x4& Lacc, float sc) {
+  const unsigned su = __float_as_uint(sc);
+  const auto sw = __builtin_amdgcn_permlane16_swap(su, su, false, false);
+  Lacc[0] *= sc;
+  Lacc[1] *= __uint_as_float(sw[1]);
+}
+
 template <typename T, int D, bool CSA>
 __global__ void __launch_bounds__(256, (sizeof(T) == 2 ? 2 : 1)) attn_fwd_kernel(FwdParams p) {
   using Chunk = typename Elem<T>::Chunk;
   constexpr bool F32 = sizeof(T) == 4;
   constexpr int EPC = Elem<T>::EPC;
   constexpr int CH = D / EPC;                // 16-byte chunks per row
+  constexpr int ROWB = CH * 16;              // bytes per row (global and LDS)
   constexpr int NSTEP = CH / 2;              // QK^T contraction steps
+  constexpr int NQK = 2 * NSTEP;             // (step, 32-key block) pairs of one S^T tile
   constexpr int NMB = (D + 31) / 32;         // 32-row blocks of O^T
-  constexpr int TILE_BYTES = kTile * CH * 16;
+  constexpr int TILE_BYTES = kTile * ROWB;
   constexpr int SWZ_MASK = CH - 1;
+  constexpr int ROUNDS = (kTile * CH + 255) / 256;
   static_assert(CH >= 2 && (CH & (CH - 1)) == 0, "chunk count must be a power of two");
 
   __shared__ __attribute__((aligned(1024))) char smem[4 * TILE_BYTES];  // K0 K1 V0 V1
@@ -212,38 +225,40 @@ __global__ void __launch_bounds__(256, (sizeof(T) == 2 ? 2 : 1)) attn_fwd_kernel
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int h = lane >> 5;
   const int n = lane & 31;
   const int Tn = p.T;
   const int BH = p.B * p.H;
-  const int bh = blockIdx.x % BH;            // heads fastest: every block of a head on one XCD
+  const int bh = blockIdx.x % BH;              // heads fastest: every block of a head on one XCD
   const int qb = p.nqb - 1 - blockIdx.x / BH;  // longest (last) query blocks first
   const int q0 = qb * kBlockRows;
-  const int qw = q0 + 32 * wave;             // first query row of this wave
-  const int qr = qw + n;                     // this lane's query row
+  const int qw = q0 + 32 * wave;               // first query row of this wave
+  const int qr = qw + n;                       // this lane's query row
   const bool wave_rows = qw < Tn;
   const int jw = wave_rows ? min(qw + 31, Tn - 1) / kTile : -1;  // last tile of this wave
   const int jmax = min(q0 + kBlockRows - 1, Tn - 1) / kTile;      // last tile of the block
 
   const size_t head = (size_t)bh * (size_t)Tn * D;
-  const T* __restrict__ Qg = (const T*)p.q + head;
-  const T* __restrict__ Kg = (const T*)p.k + head;
-  const T* __restrict__ Vg = (const T*)p.v + head;
+  const char* __restrict__ Kg = (const char*)((const T*)p.k + head);
+  const char* __restrict__ Vg = (const char*)((const T*)p.v + head);
 
-  // ---- HBM -> LDS tile copy: 16 B per lane, chunk-swizzled rows, rows past T clamped
-  auto stage = [&](int buf, const T* __restrict__ src, int tile, bool is_v) {
+  // ---- HBM -> LDS tile copy: 16 B per lane, swizzled rows, rows past T clamped.
+  // Slot (r*256 + tid) of a tile holds logical chunk slot ^ swz(row): its source
+  // byte offset inside the tile is (slot*16) ^ (swz(row) << 4) (no row padding).
+  auto stage = [&](int buf, const char* __restrict__ src, int tile, bool is_v) {
+    const char* base = src + (size_t)tile * TILE_BYTES;
+    const bool full = (tile + 1) * kTile <= Tn;
 #pragma unroll
-    for (int r = 0; r < (kTile * CH + 255) / 256; ++r) {
-      if (__builtin_amdgcn_readfirstlane(r * 256 + wave * 64) < kTile * CH) {  // wave-uniform
-        const int g = r * 256 + tid;
-        const int row = g / CH;
-        const int phys = g % CH;
-        const int logical = phys ^ ((is_v ? swz_v(row) : swz_k(row)) & SWZ_MASK);
-        const int grow = min(tile * kTile + row, Tn - 1);
-        const char* srcp = (const char*)(src + (size_t)grow * D) + logical * 16;
+    for (int r = 0; r < ROUNDS; ++r) {
+      if (r * 256 + wave * 64 < kTile * CH) {  // wave-uniform
+        const int slot = r * 256 + tid;
+        const int row = slot / CH;
+        const int sw = (is_v ? swz_v(row) : swz_k(row)) & SWZ_MASK;
+        int off = (slot * 16) ^ (sw << 4);
+        if (!full) off -= (row - min(row, Tn - 1 - tile * kTile)) * ROWB;
         CSA_LDS char* dst = lds + buf * TILE_BYTES + (r * 256 + wave * 64) * 16;
-        __builtin_amdgcn_global_load_lds((const CSA_GLOBAL void*)srcp, (CSA_LDS void*)dst, 16, 0, 0);
+        __builtin_amdgcn_global_load_lds((const CSA_GLOBAL void*)(base + off), (CSA_LDS void*)dst, 16, 0, 0);
       }
     }
   };
@@ -251,6 +266,7 @@ __global__ void __launch_bounds__(256, (sizeof(T) == 2 ? 2 : 1)) attn_fwd_kernel
   // ---- this lane's query row in registers: chunk 2i + h of row qr (the MFMA B operand)
   Chunk qreg[NSTEP];
   {
+    const T* Qg = (const T*)p.q + head;
     const int row = min(qr, Tn - 1);
 #pragma unroll
     for (int i = 0; i < NSTEP; ++i) qreg[i] = *(const Chunk*)(Qg + (size_t)row * D + (2 * i + h) * EPC);
@@ -271,26 +287,72 @@ __global__ void __launch_bounds__(256, (sizeof(T) == 2 ? 2 : 1)) attn_fwd_kernel
     a0 = hp.lo + hp.hi;
   }
 
-  // S^T tile = K_tile Q^T, two 32-key blocks
-  auto qk = [&](int buf, f32x16 (&S)[2]) {
+  // ---- per-lane LDS read offsets (bytes inside a tile buffer)
+  // K operand of step i, block 0 (block 1 is 16 rows further): row kappa(0, n),
+  // physical chunk (2i + h) ^ swz_k(row) -- the same swizzle for both blocks.
+  int koff[NSTEP];
+  {
+    const int row = kappa(0, n);
+    const int z = swz_k(row) & SWZ_MASK;
+#pragma unroll
+    for (int i = 0; i < NSTEP; ++i) koff[i] = row * ROWB + (((2 * i + h) ^ z) << 4);
+  }
+  // V^T operand (bf16, ds_read_b64_tr_b16) of d-block mb, key chunk c, read r:
+  // row 32h + 8c + 4r + e (e = (lane & 15) >> 2), column 32mb + 16 g2 + 4 (lane & 3);
+  // rows 8c + 4r share the swizzle of row 32h + e, so c and r are immediate offsets.
+  int voff[NMB];
+  {
+    const int g2 = (lane >> 4) & 1;
+    const int jl = lane & 15;
+    const int row = 32 * h + (jl >> 2);
+#pragma unroll
+    for (int mb = 0; mb < NMB; ++mb) {
+      const bool live = 32 * mb + 16 * g2 < D;  // a whole 16-lane group is in or out
+      const int col = live ? 32 * mb + 16 * g2 + 4 * (jl & 3) : 4 * (jl & 3);
+      voff[mb] = row * ROWB + (((col / EPC) ^ (swz_v(row) & SWZ_MASK)) << 4) + ((col % EPC) / 4) * 8;
+    }
+  }
+  const bool vlive_g = F32 || (16 * ((lane >> 4) & 1) < D);  // d = 16: upper 16-lane group reads nothing
+
+  // QK^T work unit q = (step i = q / 2, block b = q % 2) of the tile in buffer `buf`
+  auto kread = [&](int buf, int q) -> Chunk {
+    const int i = q >> 1, b = q & 1;
+    return *(CSA_LDS const Chunk*)(lds + buf * TILE_BYTES + b * 16 * ROWB + koff[i]);
+  };
+  auto kmfma = [&](int q, const Chunk& a, f32x16 (&S)[2]) {
+    const int i = q >> 1, b = q & 1;
+    if constexpr (F32) {
+#pragma unroll
+      for (int u = 0; u < 4; ++u) S[b] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[u], qreg[i][u], S[b], 0, 0, 0);
+    } else {
+      S[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[i], S[b], 0, 0, 0);
+    }
+  };
+  auto qk_burst = [&](int buf, f32x16 (&S)[2]) {
     S[0] = f32x16{};
     S[1] = f32x16{};
-    CSA_LDS const char* kb = lds + buf * TILE_BYTES;
+    Chunk a = kread(buf, 0);
 #pragma unroll
-    for (int i = 0; i < NSTEP; ++i) {
-#pragma unroll
-      for (int b = 0; b < 2; ++b) {
-        const int row = kappa(b, n);
-        const int phys = (2 * i + h) ^ (swz_k(row) & SWZ_MASK);
-        const Chunk a = *(CSA_LDS const Chunk*)(kb + (row * CH + phys) * 16);
-        if constexpr (F32) {
-#pragma unroll
-          for (int u = 0; u < 4; ++u) S[b] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[u], qreg[i][u], S[b], 0, 0, 0);
-        } else {
-          S[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[i], S[b], 0, 0, 0);
-        }
-      }
+    for (int q = 0; q < NQK; ++q) {
+      const Chunk cur = a;
+      if (q + 1 < NQK) a = kread(buf, q + 1);
+      kmfma(q, cur, S);
     }
+  };
+  // V^T operand of (key chunk c, d-block mb) for the bf16 path
+  auto vread = [&](int vbuf, int c, int mb) -> bf16x8 {
+    CSA_LDS const char* a1 = lds + vbuf * TILE_BYTES + voff[mb] + 8 * c * ROWB;
+    const s16x4 r1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((CSA_LDS s16x4*)a1);
+    const s16x4 r2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((CSA_LDS s16x4*)(a1 + 4 * ROWB));
+    const bf16x4 b1 = __builtin_bit_cast(bf16x4, r1);
+    const bf16x4 b2 = __builtin_bit_cast(bf16x4, r2);
+    bf16x8 A;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      A[e] = vlive_g ? b1[e] : (bf16)0.0f;
+      A[4 + e] = vlive_g ? b2[e] : (bf16)0.0f;
+    }
+    return A;
   };
 
   f32x16 O[NMB];
@@ -298,172 +360,197 @@ __global__ void __launch_bounds__(256, (sizeof(T) == 2 ? 2 : 1)) attn_fwd_kernel
   for (int mb = 0; mb < NMB; ++mb) O[mb] = f32x16{};
   // bf16: row sums of the rounded P from v_mfma_f32_16x16x32_bf16 against a 0/1
   // operand.  Its 16-lane groups g = lane/16 hold queries n' = lane%16 (g = 0, 2)
-  // and n' + 16 (g = 1, 3), so A row 0 selects groups 0 and 2 and A row 1 groups
-  // 1 and 3: C[0][n'] = l(query n'), C[1][n'] = l(query n'+16).
+  // and n' + 16 (g = 1, 3); A row 0 selects groups 0 and 2, row 1 groups 1 and 3:
+  // C[0][n'] = l(query n'), C[1][n'] = l(query n'+16).
   f32x4 Lacc = f32x4{};
+  bf16x8 ones;
+  {
+    const int m16 = lane & 15, g16 = lane >> 4;
+    const bool sel = (m16 == 0 && (g16 & 1) == 0) || (m16 == 1 && (g16 & 1) == 1);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) ones[e] = (bf16)(sel ? 1.0f : 0.0f);
+  }
   float lsum = 0.0f;        // f32: per-lane partial row sum
   float m_run = -__builtin_inff();
   float carry = 0.0f;       // left term of the next tile's first key (lanes h = 0)
   float w0 = 0.0f;          // weight of position 0 (lanes h = 0)
 
-  // ---- prologue: K_0, V_0, K_1 into LDS
-  stage(0, Kg, 0, false);
-  stage(2, Vg, 0, true);
-  if (jmax >= 1) stage(1, Kg, 1, false);
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  __syncthreads();
-
-  f32x16 Scur[2], Snext[2];
-  if (jw >= 0) qk(0, Scur);
-  __syncthreads();  // K_0's buffer is refilled in iteration 0
-
-  for (int j = 0; j <= jmax; ++j) {
-    // buffers: K_{j+1} in K[(j+1)&1], V_j in V[j&1]; refill the two free ones
-    if (j + 2 <= jmax) stage(j & 1, Kg, j + 2, false);
-    if (j + 1 <= jmax) stage(2 + ((j + 1) & 1), Vg, j + 1, true);
-
-    if (j <= jw) {
-      const bool last = (j == jw);  // the only tile that crosses this wave's diagonal
-      if (!last) qk((j + 1) & 1, Snext);
-
-      float s[32];
+  auto rescale_all = [&](float sc) {
 #pragma unroll
-      for (int kk = 0; kk < 32; ++kk) s[kk] = Scur[kk >> 4][kk & 15];
-      // key row of s[kk] is j*64 + 32h + kk; it is visible to this lane's query iff kk <= lim
-      int lim = qr - (j * kTile + 32 * h);
-      // opaque to the optimiser: otherwise "kk <= lim" is rewritten as 32 loop-invariant
-      // per-key constants compared against 64j, which costs 32 registers
-      asm volatile("" : "+v"(lim));
+    for (int mb = 0; mb < NMB; ++mb) O[mb] *= sc;
+    rescale_lacc(Lacc, sc);
+    lsum *= sc;
+    carry *= sc;
+    w0 *= sc;
+  };
 
-      // -- running maximum over the visible logits (and the right halo)
-      float mx = -__builtin_inff();
-      if (last) {
+  // running maximum over this tile's visible logits (+ position 0 on tile 0);
+  // lazy: the shift moves only when the maximum grows by more than 2^8
+  auto update_max = [&](const float (&s)[32], int j, bool last, int lim) {
+    float mx = -__builtin_inff();
+    if (last) {
 #pragma unroll
-        for (int kk = 0; kk < 32; ++kk) mx = fmaxf(mx, (kk <= lim) ? s[kk] : -__builtin_inff());
+      for (int kk = 0; kk < 32; ++kk) mx = fmaxf(mx, (kk <= lim) ? s[kk] : -__builtin_inff());
+    } else {
+#pragma unroll
+      for (int kk = 0; kk < 32; ++kk) mx = fmaxf(mx, s[kk]);
+    }
+    if (CSA && j == 0) mx = fmaxf(mx, a0);
+    const Half hm = pair_values(mx);
+    mx = fmaxf(hm.lo, hm.hi);
+    const float m_new = fmaxf(m_run, mx * kLog2e);
+    if (__builtin_amdgcn_ballot_w64(m_new > m_run + 8.0f) != 0) {
+      rescale_all(exp2_fast(m_run - m_new));
+      m_run = m_new;
+    }
+  };
+
+  // fp32 path: O^T += V^T P^T with P in float32, one MFMA per key
+  auto pv_f32 = [&](int vbuf, const float (&w)[32]) {
+    CSA_LDS const char* vb = lds + vbuf * TILE_BYTES;
+#pragma unroll
+    for (int kk = 0; kk < 32; ++kk) lsum += w[kk];
+#pragma unroll
+    for (int c = 0; c < 32; ++c) {
+      const int row = 32 * h + c;
+#pragma unroll
+      for (int mb = 0; mb < NMB; ++mb) {
+        const int col = 32 * mb + n;
+        float a = 0.0f;
+        if (col < D) {
+          const int phys = (col / EPC) ^ (swz_v(row) & SWZ_MASK);
+          a = *(CSA_LDS const float*)(vb + (row * CH + phys) * 16 + (col % EPC) * 4);
+        }
+        O[mb] = __builtin_amdgcn_mfma_f32_32x32x2f32(a, w[c], O[mb], 0, 0, 0);
+      }
+    }
+  };
+  // bf16 path: one key chunk c (keys 32h + 8c + e) of O^T += V^T P^T, plus its row sums
+  auto pack = [&](const float (&w)[32], int c) -> bf16x8 {
+    bf16x8 P;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) P[e] = (bf16)w[8 * c + e];
+    return P;
+  };
+  auto pv_burst_bf16 = [&](int vbuf, const float (&w)[32]) {
+    bf16x8 a = vread(vbuf, 0, 0);
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const bf16x8 P = pack(w, c);
+#pragma unroll
+      for (int mb = 0; mb < NMB; ++mb) {
+        const bf16x8 cur = a;
+        if (mb + 1 < NMB) a = vread(vbuf, c, mb + 1);
+        else if (c + 1 < 4) a = vread(vbuf, c + 1, 0);
+        O[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur, P, O[mb], 0, 0, 0);
+      }
+      Lacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, P, Lacc, 0, 0, 0);
+    }
+  };
+
+  // ---------------------------------------------------------------- one tile
+  // PAR = j & 1: K_{j+1} sits in K buffer 1 - PAR, V_j in V buffer PAR (LDS buffer 2 + PAR).
+  // Scur holds S^T of tile j; for a tile before the diagonal, Snext receives S^T of tile j+1.
+  auto tile = [&](auto par_c, auto last_c, int j, f32x16 (&Scur)[2], f32x16 (&Snext)[2]) {
+    constexpr int PAR = decltype(par_c)::value;
+    constexpr int KNEXT = 1 - PAR;
+    constexpr int VBUF = 2 + PAR;
+    constexpr bool last = decltype(last_c)::value;  // the only tile crossing this wave's diagonal
+    float s[32];
+#pragma unroll
+    for (int kk = 0; kk < 32; ++kk) s[kk] = Scur[kk >> 4][kk & 15];
+    // key row of s[kk] is j*64 + 32h + kk; visible to this lane's query iff kk <= lim
+    int lim = qr - (j * kTile + 32 * h);
+    // opaque: otherwise "kk <= lim" becomes 32 loop-invariant per-key constants
+    asm volatile("" : "+v"(lim));
+    update_max(s, j, last, lim);
+    float* w = s;  // finished weights overwrite the logits in place
+
+    if constexpr (!CSA) {
+      // ---------------- standard softmax attention: w = 2^(a log2 e - m), masked on the diagonal
+      if (!last) {
+        float mr = m_run;
+        asm volatile("" : "+v"(mr));
+#pragma unroll
+        for (int kk = 0; kk < 32; ++kk) w[kk] = exp2_fast(__builtin_fmaf(s[kk], kLog2e, -mr));
+        if constexpr (F32) pv_f32(VBUF, s);
+        else pv_burst_bf16(VBUF, s);
+        qk_burst(KNEXT, Snext);
       } else {
+        float mr = m_run;
+        asm volatile("" : "+v"(mr));
 #pragma unroll
-        for (int kk = 0; kk < 32; ++kk) mx = fmaxf(mx, s[kk]);
-        if (CSA && h == 0) mx = fmaxf(mx, Snext[0][0]);
+        for (int kk = 0; kk < 32; ++kk)
+          w[kk] = (kk <= lim) ? exp2_fast(__builtin_fmaf(s[kk], kLog2e, -mr)) : 0.0f;
+        if constexpr (F32) pv_f32(VBUF, s);
+        else pv_burst_bf16(VBUF, s);
       }
-      if (CSA && j == 0) mx = fmaxf(mx, a0);
-      {
-        const Half hm = pair_values(mx);
-        mx = fmaxf(hm.lo, hm.hi);
+      return;
+    } else {
+      // ---------------- continuous softmax attention
+      const float al0 = __builtin_fmaf(s[0], kLog2e, -m_run);
+      const float pv0 = exp2_fast(al0);
+      float al31 = __builtin_fmaf(s[31], kLog2e, -m_run);
+      float pv31 = exp2_fast(al31);
+      // edge (key 31, key 32) across the lane halves, computed identically by both lanes:
+      // R -> key 31 (h = 0), L -> key 32 (h = 1)
+      const Half xa0 = pair_values(al0), xp0 = pair_values(pv0);
+      const Half xa31 = pair_values(al31), xp31 = pair_values(pv31);
+      float RE1, LE1;
+      edge_terms<F32>(xa31.lo, xp31.lo, xa0.hi, xp0.hi, RE1, LE1);
+      if (j == 0) {  // position 0: only its right neighbour (eq. (10), i = 0)
+        const float a0l = __builtin_fmaf(a0, kLog2e, -m_run);
+        float R0, L1;
+        edge_terms<F32>(a0l, exp2_fast(a0l), al0, pv0, R0, L1);
+        w0 = R0;
+        carry = L1;
       }
-      const float m_new = fmaxf(m_run, mx * kLog2e);
-      // lazy rescale: keep the old shift while the maximum grows by < 2^8
-      if (__builtin_amdgcn_ballot_w64(m_new > m_run + 8.0f) != 0) {
-        const float sc = exp2_fast(m_run - m_new);
-#pragma unroll
-        for (int mb = 0; mb < NMB; ++mb) O[mb] *= sc;
-        {
-          // Lacc lanes 0..15 hold the sums of queries n' (element 0) and n' + 16
-          // (element 1): the second needs the factor of lane n' + 16.
-          const unsigned su = __float_as_uint(sc);
-          const auto sw = __builtin_amdgcn_permlane16_swap(su, su, false, false);
-          Lacc[0] *= sc;
-          Lacc[1] *= __uint_as_float(sw[1]);
-        }
-        lsum *= sc;
-        carry *= sc;
-        w0 *= sc;
-        m_run = m_new;
-      }
+      float Lprev = h == 0 ? carry : LE1;
+      float ac = al0, pc = pv0;
 
-      // s[] is overwritten in place by the finished weights w (s[kk] is dead
-      // once alpha_kk has been formed), so the chain needs only a few extra registers.
-      float* w = s;
-      if constexpr (CSA) {
-        const float al0 = __builtin_fmaf(s[0], kLog2e, -m_run);
-        const float pv0 = exp2_fast(al0);
-        const float al31 = __builtin_fmaf(s[31], kLog2e, -m_run);
-        const float pv31 = exp2_fast(al31);
-        // -- boundary edges: each lane computes the edge to the right of its key 31.
-        //    h = 0: (key 31, key 32) with key 32 from the partner lane;
-        //    h = 1: (key 63, next tile's key 0) with that halo from the partner lane.
-        float ah = al31, ph = pv31;
-        if (!last) {
-          ah = __builtin_fmaf(Snext[0][0], kLog2e, -m_run);
-          ph = exp2_fast(ah);
-        }
-        const Half xa0 = pair_values(al0), xp0 = pair_values(pv0);
-        const Half xah = pair_values(ah), xph = pair_values(ph);
-        const float ar = h == 0 ? xa0.hi : xah.lo;
-        const float pr = h == 0 ? xp0.hi : xph.lo;
-        float Rb, Lb;
-        edge_terms<F32>(al31, pv31, ar, pr, Rb, Lb);
-        // h = 0 sends L of key 32 to h = 1; h = 1 sends L of the next tile's key 0 to h = 0
-        const Half xl = pair_values(Lb);
-        const float Lrecv = h == 0 ? xl.hi : xl.lo;
-        if (j == 0) {  // position 0: only its right neighbour (eq. (10), i = 0)
-          const float a0l = __builtin_fmaf(a0, kLog2e, -m_run);
-          float R0, L1;
-          edge_terms<F32>(a0l, exp2_fast(a0l), al0, pv0, R0, L1);
-          w0 = R0;
-          carry = L1;
-        }
-        float Lprev = h == 0 ? carry : Lrecv;
-        carry = Lrecv;  // for h = 0: left term of key 64(j+1), already on this iteration's shift
-        float ac = al0, pc = pv0;
-        if (!last) {
-          // private copy of the shift: keeps the two branches from sharing (and
-          // hoisting) their 32 exponentials, which would keep them all live at once
-          float mr = m_run;
-          asm volatile("" : "+v"(mr));
+      if (!last) {
+        // private copy of the shift: the two branches must not share (and hoist) their exponentials
+        float mr = m_run;
+        asm volatile("" : "+v"(mr));
 #pragma unroll
-          for (int kk = 0; kk < 31; ++kk) {
-            float an = al31, pn = pv31;
-            if (kk + 1 < 31) {
-              an = __builtin_fmaf(s[kk + 1], kLog2e, -mr);
-              pn = exp2_fast(an);
-            }
-            edge<F32>(ac, pc, an, pn, Lprev, w[kk], Lprev);
-            ac = an;
-            pc = pn;
+        for (int kk = 0; kk < 31; ++kk) {
+          float an = al31, pn = pv31;
+          if (kk + 1 < 31) {
+            an = __builtin_fmaf(s[kk + 1], kLog2e, -mr);
+            pn = exp2_fast(an);
           }
-          w[31] = Lprev + Rb;
-        } else {
-          // diagonal tile: column t keeps only its left term, columns > t get 0
-          float mr = m_run;
-          asm volatile("" : "+v"(mr));
-#pragma unroll
-          for (int kk = 0; kk < 32; ++kk) {
-            float R = Rb, Lnext = 0.0f;
-            float an = 0.0f, pn = 0.0f;
-            if (kk < 31) {
-              an = al31;
-              pn = pv31;
-              if (kk + 1 < 31) {
-                an = __builtin_fmaf(s[kk + 1], kLog2e, -mr);
-                pn = exp2_fast(an);
-              }
-              edge_terms<F32>(ac, pc, an, pn, R, Lnext);
-            }
-            w[kk] = kk < lim ? Lprev + R : (kk == lim ? Lprev : 0.0f);
-            Lprev = Lnext;
-            ac = an;
-            pc = pn;
-          }
+          edge<F32>(ac, pc, an, pn, Lprev, w[kk], Lprev);
+          ac = an;
+          pc = pn;
         }
-      } else {
-        if (!last) {
-#pragma unroll
-          for (int kk = 0; kk < 32; ++kk) w[kk] = exp2_fast(__builtin_fmaf(s[kk], kLog2e, -m_run));
-        } else {
-#pragma unroll
-          for (int kk = 0; kk < 32; ++kk)
-            w[kk] = (kk <= lim) ? exp2_fast(__builtin_fmaf(s[kk], kLog2e, -m_run)) : 0.0f;
+        // key 31 of each lane half: h = 0 has both terms; for h = 1 (key 63) the right
+        // term needs the next tile's first logit and is added after the next QK^T
+        w[31] = Lprev + (h == 0 ? RE1 : 0.0f);
+        if constexpr (F32) pv_f32(VBUF, s);
+        else pv_burst_bf16(VBUF, s);
+        qk_burst(KNEXT, Snext);
+        // right halo: the next tile's first key (lanes h = 0 of Snext)
+        float ah = pair_values(__builtin_fmaf(Snext[0][0], kLog2e, -m_run)).lo;
+        if (__builtin_amdgcn_ballot_w64(ah > 8.0f) != 0) {
+          // rare: the halo exceeds the shift by more than 2^8 -- move the shift now
+          const float dm = fmaxf(ah, 0.0f);
+          rescale_all(exp2_fast(-dm));
+          al31 -= dm;
+          pv31 *= exp2_fast(-dm);
+          ah -= dm;
+          m_run += dm;
         }
-      }
-
-      // -- O^T += V^T P^T
-      CSA_LDS const char* vb = lds + (2 + (j & 1)) * TILE_BYTES;
-      if constexpr (F32) {
-#pragma unroll
-        for (int kk = 0; kk < 32; ++kk) lsum += w[kk];
-#pragma unroll
-        for (int c = 0; c < 32; ++c) {
-          const int row = 32 * h + c;
+        // edge (key 63, halo) computed identically by both lanes: R -> key 63 (h = 1),
+        // L -> the next tile's key 0 (kept by h = 0)
+        const Half ya31 = pair_values(al31), yp31 = pair_values(pv31);
+        float RE2, LE2;
+        edge_terms<F32>(ya31.hi, yp31.hi, ah, exp2_fast(ah), RE2, LE2);
+        carry = LE2;
+        const float r63 = h == 1 ? RE2 : 0.0f;  // weight still missing from key 63
+        if constexpr (F32) {
+          lsum += r63;
+          CSA_LDS const char* vb = lds + VBUF * TILE_BYTES;
+          const int row = 32 * h + 31;
 #pragma unroll
           for (int mb = 0; mb < NMB; ++mb) {
             const int col = 32 * mb + n;
@@ -472,56 +559,104 @@ __global__ void __launch_bounds__(256, (sizeof(T) == 2 ? 2 : 1)) attn_fwd_kernel
               const int phys = (col / EPC) ^ (swz_v(row) & SWZ_MASK);
               a = *(CSA_LDS const float*)(vb + (row * CH + phys) * 16 + (col % EPC) * 4);
             }
-            O[mb] = __builtin_amdgcn_mfma_f32_32x32x2f32(a, w[c], O[mb], 0, 0, 0);
+            O[mb] = __builtin_amdgcn_mfma_f32_32x32x2f32(a, r63, O[mb], 0, 0, 0);
           }
-        }
-      } else {
-        const int g2 = (lane >> 4) & 1;
-        const int jl = lane & 15;
-        bf16x8 ones;
-        {
-          const int m16 = lane & 15, g16 = lane >> 4;
-          const bool sel = (m16 == 0 && (g16 & 1) == 0) || (m16 == 1 && (g16 & 1) == 1);
+        } else {
+          // rank-1 update: key chunk 3 with only key 63 (element 7 of lanes h = 1) non-zero
+          bf16x8 P3;
 #pragma unroll
-          for (int e = 0; e < 8; ++e) ones[e] = (bf16)(sel ? 1.0f : 0.0f);
-        }
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          bf16x8 P;
-#pragma unroll
-          for (int e = 0; e < 8; ++e) P[e] = (bf16)w[8 * c + e];
+          for (int e = 0; e < 8; ++e) P3[e] = (bf16)0.0f;
+          P3[7] = (bf16)r63;
+          bf16x8 a = vread(VBUF, 3, 0);
 #pragma unroll
           for (int mb = 0; mb < NMB; ++mb) {
-            bf16x8 A;
-            const int col = 32 * mb + 16 * g2 + 4 * (jl & 3);
-            const bool live = 32 * mb + 16 * g2 < D;  // whole 16-lane group in or out
-            const int colc = live ? col : 4 * (jl & 3);
-            const int row1 = 32 * h + 8 * c + (jl >> 2);
-            const int row2 = row1 + 4;
-            const int byte = ((colc % EPC) / 4) * 8;
-            CSA_LDS const char* a1 = vb + (row1 * CH + ((colc / EPC) ^ (swz_v(row1) & SWZ_MASK))) * 16 + byte;
-            CSA_LDS const char* a2 = vb + (row2 * CH + ((colc / EPC) ^ (swz_v(row2) & SWZ_MASK))) * 16 + byte;
-            const s16x4 r1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((CSA_LDS s16x4*)a1);
-            const s16x4 r2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((CSA_LDS s16x4*)a2);
-            const bf16x4 b1 = __builtin_bit_cast(bf16x4, r1);
-            const bf16x4 b2 = __builtin_bit_cast(bf16x4, r2);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              A[e] = live ? b1[e] : (bf16)0.0f;
-              A[4 + e] = live ? b2[e] : (bf16)0.0f;
-            }
-            O[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, P, O[mb], 0, 0, 0);
+            const bf16x8 cur = a;
+            if (mb + 1 < NMB) a = vread(VBUF, 3, mb + 1);
+            O[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur, P3, O[mb], 0, 0, 0);
           }
-          Lacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, P, Lacc, 0, 0, 0);
+          Lacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, P3, Lacc, 0, 0, 0);
         }
-      }
-      if (!last) {
-        Scur[0] = Snext[0];
-        Scur[1] = Snext[1];
+      } else {
+        // diagonal tile: column t keeps only its left term, columns > t get 0
+        float mr = m_run;
+        asm volatile("" : "+v"(mr));
+#pragma unroll
+        for (int kk = 0; kk < 32; ++kk) {
+          float R = 0.0f, Lnext = 0.0f;
+          float an = 0.0f, pn = 0.0f;
+          if (kk < 31) {
+            an = al31;
+            pn = pv31;
+            if (kk + 1 < 31) {
+              an = __builtin_fmaf(s[kk + 1], kLog2e, -mr);
+              pn = exp2_fast(an);
+            }
+            edge_terms<F32>(ac, pc, an, pn, R, Lnext);
+          } else {
+            R = RE1;  // key 31 (h = 0); key 63 (h = 1) is never left of a visible key here
+          }
+          w[kk] = kk < lim ? Lprev + R : (kk == lim ? Lprev : 0.0f);
+          Lprev = Lnext;
+          ac = an;
+          pc = pn;
+        }
+        if constexpr (F32) pv_f32(VBUF, s);
+        else pv_burst_bf16(VBUF, s);
       }
     }
+  };
+
+  // ---- prologue: K_0, V_0, K_1 into LDS; S^T of tile 0
+  stage(0, Kg, 0, false);
+  stage(2, Vg, 0, true);
+  if (jmax >= 1) stage(1, Kg, 1, false);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  f32x16 SA[2], SB[2];
+  if (jw >= 0) qk_burst(0, SA);
+  __syncthreads();  // K_0's buffer is refilled in iteration 0
+
+  // ---- main loop.  Every wave runs one iteration (one barrier) per key tile of the
+  // block, j = 0..jmax, but computes only on its own tiles: j < jw before its diagonal
+  // (unrolled by two so that every LDS buffer offset is a constant), then j = jw.
+  // Iteration j refills K buffer j&1 with K_{j+2} and V buffer (j+1)&1 with V_{j+1}.
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  using BF = std::integral_constant<bool, false>;
+  using BT = std::integral_constant<bool, true>;
+  auto refill = [&](int j) {
+    if (j + 2 <= jmax) stage(j & 1, Kg, j + 2, false);
+    if (j + 1 <= jmax) stage(2 + ((j + 1) & 1), Vg, j + 1, true);
+  };
+  auto sync = [&]() {
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
+  };
+  int j = 0;
+  for (; j + 1 < jw; j += 2) {
+    refill(j);
+    tile(I0{}, BF{}, j, SA, SB);
+    sync();
+    refill(j + 1);
+    tile(I1{}, BF{}, j + 1, SB, SA);
+    sync();
+  }
+  if (j < jw) {  // j even
+    refill(j);
+    tile(I0{}, BF{}, j, SA, SB);
+    sync();
+    ++j;
+  }
+  if (j == jw) {
+    refill(j);
+    if ((j & 1) == 0) tile(I0{}, BT{}, j, SA, SB);
+    else tile(I1{}, BT{}, j, SB, SA);
+    sync();
+    ++j;
+  }
+  for (; j <= jmax; ++j) {
+    refill(j);
+    sync();
   }
 
   if (!wave_rows) return;
@@ -534,9 +669,8 @@ __global__ void __launch_bounds__(256, (sizeof(T) == 2 ? 2 : 1)) attn_fwd_kernel
     const Half hl = pair_values(lsum);
     l = hl.lo + hl.hi;
   } else {
-    // l(query n) sits in lane n % 16, register n / 16 (C layout of the 16x16 MFMA)
-    // (elements are copied to scalars first: __builtin_bit_cast of an ext_vector
-    // element reads element 0 with this compiler)
+    // l(query n) sits in lane n % 16, element n / 16 of Lacc.  (Elements are copied
+    // to scalars first: __builtin_bit_cast of an ext_vector element reads element 0.)
     const int src = n & 15;
     const float s0 = Lacc[0], s1 = Lacc[1];
     const float c0 = __int_as_float(__builtin_amdgcn_ds_bpermute(src << 2, __float_as_int(s0)));

@@ -1,0 +1,553 @@
+// bf16 causal attention forward for gfx950 on 16x16x32 MFMAs: continuous softmax
+// attention (CSA = true) and standard softmax attention on the identical tiling.
+//
+// Method: J. Su, "Continuous Softmax Attention", eq. (10)-(11) -- see attn_fwd.hpp
+// for the correction-weight arithmetic ("p-form"), which is shared.
+//
+// Why a second tiling.  With 32 queries per wave (32x32 MFMAs) the accumulator of
+// O^T alone takes 64 VGPRs and the kernel needs ~244, which caps the SIMD at two
+// waves; the correction weights are VALU work, a wave issues at most one VALU
+// instruction every 4 cycles and a second wave is needed to fill the other issue
+// slot, so latency (exp/rcp, LDS, MFMA results, barriers) goes unhidden.  Here a
+// wave owns 16 queries: O^T is 32 VGPRs, Q 16, S 16, and four waves fit per SIMD.
+//
+// Work decomposition
+//   * One work-group = 8 waves = 128 query rows of one (b, h); wave w owns rows
+//     q0 + 16w .. +15.  Key tiles are 64 rows of k, double-buffered in LDS.
+//   * S^T = K Q^T with v_mfma_f32_16x16x32_bf16, four 16-key blocks per tile.
+//     Lane (n, g) -- n = lane % 16 (query), g = lane / 16 -- receives rows 4g..4g+3
+//     of each block; the K operand rows are permuted so that these are keys
+//     16g + 4b + r: every lane holds 16 CONSECUTIVE keys of its query, and the
+//     four lanes of a query hold the tile in order.  The neighbour stencil of
+//     eq. (10) is in-register except at the three group boundaries (exchanged with
+//     ds_bpermute) and at the tile's right edge, whose neighbour -- the next tile's
+//     first key -- comes from computing block 0 of the next tile's S^T early.
+//   * O^T += V^T P^T on 16x16x32 MFMAs with P (bf16) straight from registers
+//     (lane (n, g) holds keys 16g + 8c + e of query n for key chunk c), V^T via
+//     ds_read_b64_tr_b16.  Row sums take the same bf16-rounded P (v_dot2_f32_bf16
+//     against (1, 1)), so numerator and denominator see identical weights.
+//
+// LDS layouts (16-byte chunks, both filled by global_load_lds_dwordx4; every
+// copy instruction of a wave reads whole 64-byte row segments from HBM):
+//   K tile: one region per contraction step (4 chunks x 64 rows = 4 KiB); inside
+//           it, row r sits in 64-byte slot 4 (r & 3) + (r >> 4) + 16 ((r >> 2) & 3)
+//           with its chunk cc at position cc ^ (r & 3).  This is the placement
+//           that measured free of LDS bank conflicts for the 16 rows one lane group
+//           reads for an MFMA A operand (a plain XOR by r >> 4 was not), and every
+//           K address is one per-lane base plus an immediate.
+//   V tile: one region per 32 d-columns (4 chunks x 64 rows); chunk cc of row r at
+//           position cc ^ 2 bit4(r), so the two half-waves of a transposed read use
+//           disjoint banks; one per-lane base per parity of the 16-column block.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <type_traits>
+
+#include "attn_fwd.hpp"
+
+namespace csa {
+
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kWaves16 = 8;  // 8 waves x 16 queries = 128 rows, as kBlockRows
+
+// One 16-byte HBM -> LDS copy per lane (global_load_lds_dwordx4): lane i reads
+// base + voff and writes LDS address lds_addr + 16 i (no instruction offset: it would
+// move the LDS destination as well).  Issued as inline asm so that the compiler does
+// not track it: it would otherwise make every later transposed LDS read wait for all
+// copies in flight (it cannot tell the buffers apart).  Completion is awaited
+// explicitly (s_waitcnt vmcnt(0) and a barrier) before any wave reads the destination.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void lds_copy16(const char* base, int voff, unsigned lds_addr) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+               :
+               : "v"(voff), "s"(base), "s"(lds_addr)
+               : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+// s_waitcnt vmcnt(0) as an instruction the compiler sees (so it also knows that its
+// own loads, e.g. of Q, have completed and adds no later waits for them).
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+// Edge (t, t+1) of eq. (10) from p_t, p_{t+1}, y = alpha_{t+1} - alpha_t and u = 1/y,
+// in the p-form of attn_fwd.hpp (bf16 outputs: Taylor branch below |y| < 0.07).
+// Returns w_left = Lprev + (right term of t) and the left term of t+1.
+__device__ __forceinline__ void edge_yu(float pl, float pr, float y, float u, float Lprev,
+                                        float& w_left, float& L_right) {
+  const float du = (pr - pl) * u;
+  const float wr = __builtin_fmaf(__builtin_fmaf(-kLn2, pl, du), u, Lprev);
+  const float lr = __builtin_fmaf(kLn2, pr, -du) * u;
+  float gp, gm;
+  Taylor<false>::eval(y, gp, gm);
+  const float wt = __builtin_fmaf(pl, gp, Lprev);
+  const float lt = pr * gm;
+  const bool small = __builtin_fabsf(y) < Taylor<false>::Y0;
+  w_left = small ? wt : wr;
+  L_right = small ? lt : lr;
+}
+
+template <int D, bool CSA>
+__global__ void __launch_bounds__(512, 4) attn16_kernel(FwdParams p) {
+  static_assert(D == 16 || D == 64 || D == 128, "head dimension");
+  constexpr int CH = D / 8;                      // 16-byte chunks per row
+  constexpr int ROWB = D * 2;                    // bytes per row in HBM
+  constexpr int NSTEP = D >= 32 ? D / 32 : 1;    // QK^T contraction steps (32 d each)
+  constexpr int NMB = D / 16;                    // 16-row blocks of O^T
+  constexpr int TILE_BYTES = kTile * ROWB;
+  constexpr int SLOTS = kTile * CH;              // 16-byte slots per tile
+  constexpr int ROUNDS = (SLOTS + 511) / 512;
+  constexpr int RW = CH < 4 ? CH : 4;            // chunks per row segment of a region
+  constexpr int REGION = 64 * RW * 16;           // bytes per region
+
+  __shared__ __attribute__((aligned(1024))) char smem[4 * TILE_BYTES];  // K0 K1 V0 V1
+  CSA_LDS char* lds = (CSA_LDS char*)smem;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int n = lane & 15;   // query of this lane within the wave
+  const int g = lane >> 4;   // lane group: keys 16g .. 16g+15 of every tile
+  const int Tn = p.T;
+  const int BH = p.B * p.H;
+  const int bh = blockIdx.x % BH;              // heads fastest: every block of a head on one XCD
+  const int qb = p.nqb - 1 - blockIdx.x / BH;  // longest (last) query blocks first
+  const int q0 = qb * kBlockRows;
+  const int qw = q0 + 16 * wave;
+  const int qr = qw + n;
+  const bool wave_rows = qw < Tn;
+  const int jw = wave_rows ? min(qw + 15, Tn - 1) / kTile : -1;  // last tile of this wave
+  const int jmax = min(q0 + kBlockRows - 1, Tn - 1) / kTile;      // last tile of the block
+
+  const size_t head = (size_t)bh * (size_t)Tn * D;
+  const char* __restrict__ Kg = (const char*)((const bf16*)p.k + head);
+  const char* __restrict__ Vg = (const char*)((const bf16*)p.v + head);
+
+  // ---- HBM -> LDS: slot sigma = round*512 + tid of a tile; its source (row, chunk)
+  // under the K or V layout above, as a byte offset inside the tile's rows.
+  auto ksrc = [&](int sigma) {
+    const int region = sigma / (64 * RW);  // contraction step
+    const int within = sigma % (64 * RW);
+    const int gi = within / RW;            // row segment slot: 4 (r & 3) + (r >> 4) + 16 ((r >> 2) & 3)
+    const int row = 16 * (gi & 3) + 4 * (gi >> 4) + ((gi >> 2) & 3);
+    const int cc = (within % RW) ^ (row & (RW - 1));
+    return row * ROWB + (region * RW + cc) * 16;
+  };
+  auto vsrc = [&](int sigma) {
+    const int region = sigma / (64 * RW);  // 32 d-columns
+    const int within = sigma % (64 * RW);
+    const int row = within / RW;
+    const int cc = (within % RW) ^ ((2 * ((row >> 4) & 1)) & (RW - 1));
+    return row * ROWB + (region * RW + cc) * 16;
+  };
+  // round r of a copy reads the same rows as round 0, 8 chunks (128 bytes) further
+  const int koffg = ksrc(tid), voffg = vsrc(tid);
+  auto stage = [&](int buf, const char* __restrict__ src, int tile, bool is_v) {
+    const char* base = src + (size_t)tile * TILE_BYTES;
+    const int rows_left = Tn - tile * kTile;  // >= 1
+    int off = is_v ? voffg : koffg;
+    if (rows_left < kTile) {  // last tile of the sequence: clamp rows past T
+      const int row = off / ROWB;
+      off -= (row - min(row, rows_left - 1)) * ROWB;
+    }
+#pragma unroll
+    for (int r = 0; r < ROUNDS; ++r) {
+      if (r * 512 + wave * 64 < SLOTS) {  // wave-uniform
+        const unsigned dst = __builtin_amdgcn_readfirstlane(
+            (unsigned)(uintptr_t)(lds + buf * TILE_BYTES + (r * 512 + wave * 64) * 16));
+        lds_copy16(base + 128 * r, off, dst);
+      }
+    }
+  };
+
+  // ---- Q operand in registers: qreg[s] = chunk 4s + g of row qr (zero past d)
+  bf16x8 qreg[NSTEP];
+  {
+    const bf16* Qg = (const bf16*)p.q + head;
+    const int row = min(qr, Tn - 1);
+#pragma unroll
+    for (int s = 0; s < NSTEP; ++s) {
+      if (4 * s + g < CH) {
+        qreg[s] = *(const bf16x8*)(Qg + (size_t)row * D + (4 * s + g) * 8);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) qreg[s][e] = (bf16)0.0f;
+      }
+    }
+  }
+
+  // query-wide reductions over the four lane groups (lanes n, n+16, n+32, n+48)
+  auto qmax = [&](float x) {
+    const unsigned u = __float_as_uint(x);
+    const auto r16 = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+    x = fmaxf(__uint_as_float(r16[0]), __uint_as_float(r16[1]));
+    const Half h32 = pair_values(x);
+    return fmaxf(h32.lo, h32.hi);
+  };
+  auto qsum = [&](float x) {
+    const unsigned u = __float_as_uint(x);
+    const auto r16 = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+    x = __uint_as_float(r16[0]) + __uint_as_float(r16[1]);
+    const Half h32 = pair_values(x);
+    return h32.lo + h32.hi;
+  };
+  auto from_lane = [&](int src, float x) {  // value of x in lane src
+    return __int_as_float(__builtin_amdgcn_ds_bpermute(src << 2, __float_as_int(x)));
+  };
+  const int lane_dn = (lane + 16) & 63;  // same query, next lane group
+  const int lane_up = (lane - 16) & 63;  // same query, previous lane group
+
+  // ---- logit of position 0: a0 = q . k0 (zero when k0 is null)
+  float a0 = 0.0f;
+  if (CSA && p.k0 != nullptr) {
+    const bf16* K0 = (const bf16*)p.k0 + (size_t)bh * D;
+    float part = 0.0f;
+#pragma unroll
+    for (int s = 0; s < NSTEP; ++s) {
+      if (4 * s + g < CH) {
+        const bf16x8 kc = *(const bf16x8*)(K0 + (4 * s + g) * 8);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) part = __builtin_fmaf((float)qreg[s][e], (float)kc[e], part);
+      }
+    }
+    a0 = qsum(part);
+  }
+
+  // ---- LDS read bases
+  // K operand (block b, step s): row 16(n >> 2) + 4b + (n & 3), chunk 4s + g (for d = 16,
+  // lanes g >= 2 re-read chunk g - 2 against zero Q)  ->  kbase + s*REGION + b*16*RW*16
+  const int kbase = (4 * (n & 3) + (n >> 2)) * RW * 16 + 16 * ((g & (RW - 1)) ^ (n & (RW - 1)));
+  // V^T operand (d-block mb, key chunk c, read rd): row 16g + 8c + 4rd + (n >> 2), column
+  // 16mb + 4(n & 3)  ->  vbase[mb & 1] + (mb*2 / RW)*REGION + (8c + 4rd)*RW*16
+  int vbase[2];
+#pragma unroll
+  for (int par = 0; par < 2; ++par) {
+    const int cc = ((2 * par) & (RW - 1)) + ((n >> 1) & 1);
+    vbase[par] = (16 * g + (n >> 2)) * RW * 16 + 16 * (cc ^ ((2 * (g & 1)) & (RW - 1))) + 8 * (n & 1);
+  }
+
+  auto kread = [&](int buf, int s, int b) -> bf16x8 {
+    return *(CSA_LDS const bf16x8*)(lds + buf * TILE_BYTES + kbase + s * REGION + b * 16 * RW * 16);
+  };
+  auto vread = [&](int vbuf, int c, int mb) -> bf16x8 {
+    CSA_LDS const char* a = lds + vbuf * TILE_BYTES + vbase[mb & 1] + (2 * mb / RW) * REGION + 8 * c * RW * 16;
+    const s16x4 r1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((CSA_LDS s16x4*)a);
+    const s16x4 r2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((CSA_LDS s16x4*)(a + 4 * RW * 16));
+    const bf16x4 b1 = __builtin_bit_cast(bf16x4, r1);
+    const bf16x4 b2 = __builtin_bit_cast(bf16x4, r2);
+    return bf16x8{b1[0], b1[1], b1[2], b1[3], b2[0], b2[1], b2[2], b2[3]};
+  };
+  // S^T blocks [b0, b1) of a tile, contraction steps pipelined one operand ahead
+  auto qk = [&](int buf, f32x4 (&S)[4], int b0, int b1) {
+#pragma unroll
+    for (int b = b0; b < b1; ++b) S[b] = f32x4{};
+    bf16x8 a = kread(buf, 0, b0);
+#pragma unroll
+    for (int b = b0; b < b1; ++b) {
+#pragma unroll
+      for (int s = 0; s < NSTEP; ++s) {
+        const bf16x8 cur = a;
+        if (s + 1 < NSTEP) a = kread(buf, s + 1, b);
+        else if (b + 1 < b1) a = kread(buf, 0, b + 1);
+        S[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(cur, qreg[s], S[b], 0, 0, 0);
+      }
+    }
+  };
+
+  f32x4 O[NMB];
+#pragma unroll
+  for (int mb = 0; mb < NMB; ++mb) O[mb] = f32x4{};
+  float lsum = 0.0f;     // this lane's share of the row sum of the rounded P
+  float m_run = -__builtin_inff();
+  float carry = 0.0f;   // lanes g = 3: left term of the next tile's first key
+  float w0 = 0.0f;      // lanes g = 0: weight of position 0
+
+  auto rescale_all = [&](float sc) {
+#pragma unroll
+    for (int mb = 0; mb < NMB; ++mb) O[mb] *= sc;
+    lsum *= sc;
+    carry *= sc;
+    w0 *= sc;
+  };
+
+  // ---------------------------------------------------------------- one tile
+  // PAR = j & 1: K_{j+1} sits in K buffer 1 - PAR, V_j in V buffer PAR (LDS buffer 2 + PAR).
+  // Scur holds S^T of tile j; a tile before the diagonal computes S^T of tile j+1 into Snext.
+  //
+  // The weights are produced in 16 steps, one key per step (its exponential and, for
+  // CSA, the reciprocal of the next neighbour difference one step ahead).  The tile's
+  // MFMAs are pinned between the steps: the next tile's S^T (blocks 1..3) during steps
+  // 0..7, P V of keys 0..7 during steps 8..15, the rest after; so every wave keeps the
+  // matrix cores busy while its VALU works, instead of alternating the two.
+  auto tile = [&](auto par_c, auto last_c, auto first_c, int j, f32x4 (&Scur)[4], f32x4 (&Snext)[4]) {
+    constexpr int PAR = decltype(par_c)::value;
+    constexpr int KNEXT = 1 - PAR;
+    constexpr int VBUF = 2 + PAR;
+    constexpr bool last = decltype(last_c)::value;  // the tile holding this wave's diagonal
+    const bool first = decltype(first_c)::value || (last && j == 0);
+    constexpr int NQ = 3 * NSTEP;  // MFMAs of S^T blocks 1..3 of the next tile
+    constexpr int NP = NMB + 1;    // units of one key chunk of P V: NMB MFMAs, then the row sums
+
+    // block 0 of the next tile first: its key 0 is the right halo of this tile
+    if constexpr (!last) qk(KNEXT, Snext, 0, 1);
+    float s[16];
+#pragma unroll
+    for (int t = 0; t < 16; ++t) s[t] = Scur[t >> 2][t & 3];
+    // key row of s[t] is j*64 + 16g + t; visible to this lane's query iff t <= lim
+    int lim = qr - (j * kTile + 16 * g);
+    asm volatile("" : "+v"(lim));  // opaque: keeps "t <= lim" from becoming 16 constants
+
+    // -- running maximum (lazy: the shift moves only when the maximum grows by > 2^8)
+    float mx = -__builtin_inff();
+    if constexpr (last) {
+#pragma unroll
+      for (int t = 0; t < 16; ++t) mx = fmaxf(mx, (t <= lim) ? s[t] : -__builtin_inff());
+    } else {
+#pragma unroll
+      for (int t = 0; t < 16; ++t) mx = fmaxf(mx, s[t]);
+    }
+    float halo = 0.0f;
+    if constexpr (CSA && !last) {
+      halo = from_lane(n, Snext[0][0]);  // key 0 of tile j+1 (lane n, g = 0)
+      mx = fmaxf(mx, halo);
+    }
+    if (CSA && first) mx = fmaxf(mx, a0);
+    mx = qmax(mx);
+    {
+      const float m_new = fmaxf(m_run, mx * kLog2e);
+      if (__builtin_amdgcn_ballot_w64(m_new > m_run + 8.0f) != 0) {
+        rescale_all(exp2_fast(m_run - m_new));
+        m_run = m_new;
+      }
+    }
+    float mr = m_run;
+    asm volatile("" : "+v"(mr));  // each path keeps its own exponentials
+    float* w = s;                 // finished weights overwrite the logits in place
+    auto alpha = [&](int t) { return __builtin_fmaf(s[t], kLog2e, -mr); };
+
+    // -- MFMA work placed between the weight steps
+    bf16x8 ak, av, P0;
+    if constexpr (!last) ak = kread(KNEXT, 0, 1);
+    auto qk_unit = [&](int u) {
+      const int b = 1 + u / NSTEP, st = u % NSTEP;
+      const bf16x8 cur = ak;
+      if (u + 1 < NQ) ak = kread(KNEXT, (u + 1) % NSTEP, 1 + (u + 1) / NSTEP);
+      Snext[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(cur, qreg[st], st == 0 ? f32x4{} : Snext[b], 0, 0, 0);
+    };
+    auto pv_unit = [&](int c, int u, const bf16x8& P) {
+      if (u < NMB) {
+        const bf16x8 cur = av;
+        if (u + 1 < NMB) av = vread(VBUF, c, u + 1);
+        else if (c == 0) av = vread(VBUF, 1, 0);  // first operand of the second chunk
+        O[u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(cur, P, O[u], 0, 0, 0);
+      } else {  // row sums of the same rounded P as the numerator
+        const bf16x2 one2 = {(bf16)1.0f, (bf16)1.0f};
+#pragma unroll
+        for (int e = 0; e < 8; e += 2)
+          lsum = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{P[e], P[e + 1]}, one2, lsum, false);
+      }
+    };
+    auto pack = [&](int c) {
+      bf16x8 P;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) P[e] = (bf16)w[8 * c + e];
+      return P;
+    };
+    auto slot = [&](int t) {  // after weight step t
+      if (!last && t < 8) {
+#pragma unroll
+        for (int u = t * NQ / 8; u < (t + 1) * NQ / 8; ++u) qk_unit(u);
+      }
+      if (t == 6) av = vread(VBUF, 0, 0);
+      if (t == 7) P0 = pack(0);
+      if (t >= 8) {
+#pragma unroll
+        for (int u = (t - 8) * NP / 8; u < (t - 7) * NP / 8; ++u) pv_unit(0, u, P0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    };
+
+    if constexpr (!CSA) {
+#pragma unroll
+      for (int t = 0; t < 16; ++t) {
+        const float e = exp2_fast(alpha(t));
+        w[t] = (!last || t <= lim) ? e : 0.0f;
+        slot(t);
+      }
+    } else {
+      const float al0 = alpha(0);
+      const float pv0 = exp2_fast(al0);
+      const float al15 = alpha(15);
+      const float pv15 = exp2_fast(al15);
+      // right neighbour of key 15: the next group's key 0, or (g = 3) the halo
+      float ar = from_lane(lane_dn, al0);
+      float pr = from_lane(lane_dn, pv0);
+      if (!last) {
+        const float ah = __builtin_fmaf(halo, kLog2e, -mr);
+        if (g == 3) {
+          ar = ah;
+          pr = exp2_fast(ah);
+        }
+      }
+      float R15, Lnext;
+      edge_terms<false>(al15, pv15, ar, pr, R15, Lnext);
+      // left term of key 0: from the previous group, or (g = 0) carried from the
+      // previous tile's group 3, or (first tile) from the edge with position 0
+      const float Lsend = g == 3 ? carry : Lnext;
+      float Lprev = from_lane(lane_up, Lsend);
+      carry = Lnext;  // lanes g = 3: left term of key 64(j+1)
+      if (first) {    // position 0: only its right neighbour (eq. (10), i = 0)
+        const float a0l = __builtin_fmaf(a0, kLog2e, -mr);
+        float R0, L1;
+        edge_terms<false>(a0l, exp2_fast(a0l), al0, pv0, R0, L1);
+        w0 = R0;
+        if (g == 0) Lprev = L1;
+      }
+      // edge (t, t+1) needs p_t, p_{t+1}, y_t = alpha_{t+1} - alpha_t and 1/y_t; the
+      // values of key t+2 are formed one step ahead
+      float pc = pv0;
+      float an = alpha(1), pn = exp2_fast(an);
+      float yc = an - al0, uc = __builtin_amdgcn_rcpf(yc);
+#pragma unroll
+      for (int t = 0; t < 16; ++t) {
+        if (t < 15) {
+          float ann = 0.0f, pnn = 0.0f, yn = 0.0f, un = 0.0f;
+          if (t + 2 < 15) {
+            ann = alpha(t + 2);
+            pnn = exp2_fast(ann);
+          } else if (t + 2 == 15) {
+            ann = al15;
+            pnn = pv15;
+          }
+          if (t + 2 <= 15) {
+            yn = ann - an;
+            un = __builtin_amdgcn_rcpf(yn);
+          }
+          if constexpr (!last) {
+            edge_yu(pc, pn, yc, uc, Lprev, w[t], Lprev);
+          } else {  // diagonal tile: column t keeps only its left term, columns > t get 0
+            float R, L;
+            edge_yu(pc, pn, yc, uc, 0.0f, R, L);
+            w[t] = t < lim ? Lprev + R : (t == lim ? Lprev : 0.0f);
+            Lprev = L;
+          }
+          pc = pn;
+          yc = yn;
+          uc = un;
+          an = ann;
+          pn = pnn;
+        } else {
+          w[15] = last ? (15 < lim ? Lprev + R15 : (15 == lim ? Lprev : 0.0f)) : Lprev + R15;
+        }
+        slot(t);
+      }
+    }
+    // P V of keys 8..15 of every lane group
+    const bf16x8 P1 = pack(1);
+#pragma unroll
+    for (int u = 0; u < NP; ++u) pv_unit(1, u, P1);
+  };
+
+  // ---- prologue: K_0, V_0, K_1 into LDS; S^T of tile 0
+  stage(0, Kg, 0, false);
+  stage(2, Vg, 0, true);
+  if (jmax >= 1) stage(1, Kg, 1, false);
+  wait_vmem();
+  __syncthreads();
+  f32x4 SA[4], SB[4];
+  if (jw >= 0) qk(0, SA, 0, 4);
+  __syncthreads();  // K_0's buffer is refilled in iteration 0
+
+  // ---- main loop: one iteration (one barrier) per key tile of the block for every
+  // wave; computation only on the wave's own tiles, the diagonal one last.
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  using BF = std::integral_constant<bool, false>;
+  using BT = std::integral_constant<bool, true>;
+  auto refill = [&](int j) {
+    if (j + 2 <= jmax) stage(j & 1, Kg, j + 2, false);
+    if (j + 1 <= jmax) stage(2 + ((j + 1) & 1), Vg, j + 1, true);
+  };
+  auto sync = [&]() {
+    wait_vmem();
+    __syncthreads();
+  };
+  int j = 0;
+  if (jw > 0) {  // tile 0 also takes the edge with position 0
+    refill(0);
+    tile(I0{}, BF{}, BT{}, 0, SA, SB);
+    sync();
+    j = 1;
+  }
+  for (; j + 1 < jw; j += 2) {  // j odd
+    refill(j);
+    tile(I1{}, BF{}, BF{}, j, SB, SA);
+    sync();
+    refill(j + 1);
+    tile(I0{}, BF{}, BF{}, j + 1, SA, SB);
+    sync();
+  }
+  if (j < jw) {  // j odd
+    refill(j);
+    tile(I1{}, BF{}, BF{}, j, SB, SA);
+    sync();
+    ++j;
+  }
+  if (j == jw) {
+    refill(j);
+    if ((j & 1) == 0) tile(I0{}, BT{}, BF{}, j, SA, SB);
+    else tile(I1{}, BT{}, BF{}, j, SB, SA);
+    sync();
+    ++j;
+  }
+  for (; j <= jmax; ++j) {
+    refill(j);
+    sync();
+  }
+
+  if (!wave_rows) return;
+
+  // ---- epilogue: position-0 term, normalisation, stores
+  float l = qsum(lsum);
+  float w0q = 0.0f;
+  if (CSA) {
+    w0q = from_lane(n, w0);
+    l += w0q;
+  }
+  const float inv = 1.0f / l;
+  if (qr < Tn) {
+    const bf16* V0 = (CSA && p.v0 != nullptr) ? (const bf16*)p.v0 + (size_t)bh * D : nullptr;
+    bf16* Og = (bf16*)p.out + head + (size_t)qr * D;
+#pragma unroll
+    for (int mb = 0; mb < NMB; ++mb) {
+      const int d0 = 16 * mb + 4 * g;
+      float o4[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        float acc = O[mb][r];
+        if (V0) acc = __builtin_fmaf(w0q, (float)V0[d0 + r], acc);
+        o4[r] = acc * inv;
+      }
+      *(bf16x4*)(Og + d0) = bf16x4{(bf16)o4[0], (bf16)o4[1], (bf16)o4[2], (bf16)o4[3]};
+    }
+    if (p.lse != nullptr && g == 0) {
+      const float corr = CSA ? 0.7330258411633287f : 0.0f;  // -2 ln(ln 2)
+      p.lse[(size_t)bh * Tn + qr] = (m_run + __builtin_amdgcn_logf(l)) * kLn2 + corr;
+    }
+  }
+}
+
+template <int D, bool CSA>
+inline hipError_t launch_attn16(const FwdParams& prm, hipStream_t stream) {
+  const int nqb = (prm.T + kBlockRows - 1) / kBlockRows;
+  FwdParams p = prm;
+  p.nqb = nqb;
+  const dim3 grid((unsigned)(nqb * prm.B * prm.H));
+  hipLaunchKernelGGL((attn16_kernel<D, CSA>), grid, dim3(64 * kWaves16), 0, stream, p);
+  return hipGetLastError();
+}
+
+}  // namespace csa

@@ -1,6 +1,7 @@
 // C-ABI entry points of libcsa: csa_forward and its validation.
 #include <hip/hip_runtime.h>
 
+#include "attn16.hpp"
 #include "attn_fwd.hpp"
 #include "csa.h"
 #include "validate.hpp"
@@ -15,9 +16,9 @@ int dispatch(const csa::FwdParams& p, int64_t d, int dtype, hipStream_t s) {
     else if (d == 64) e = csa::launch_attn<float, 64, CSA>(p, s);
     else e = csa::launch_attn<float, 128, CSA>(p, s);
   } else {
-    if (d == 16) e = csa::launch_attn<csa::bf16, 16, CSA>(p, s);
-    else if (d == 64) e = csa::launch_attn<csa::bf16, 64, CSA>(p, s);
-    else e = csa::launch_attn<csa::bf16, 128, CSA>(p, s);
+    if (d == 16) e = csa::launch_attn16<16, CSA>(p, s);
+    else if (d == 64) e = csa::launch_attn16<64, CSA>(p, s);
+    else e = csa::launch_attn16<128, CSA>(p, s);
   }
   return e == hipSuccess ? CSA_OK : CSA_ERR_HIP;
 }

@@ -1,6 +1,7 @@
 // C-ABI entry points of libcsa_bench: standard causal attention on the CSA tiling.
 #include <hip/hip_runtime.h>
 
+#include "attn16.hpp"
 #include "attn_fwd.hpp"
 #include "csa_bench.h"
 #include "validate.hpp"
@@ -23,9 +24,9 @@ extern "C" int std_fwd(const void* q, const void* k, const void* v, void* out, f
     else if (d == 64) e = csa::launch_attn<float, 64, false>(p, s);
     else e = csa::launch_attn<float, 128, false>(p, s);
   } else {
-    if (d == 16) e = csa::launch_attn<csa::bf16, 16, false>(p, s);
-    else if (d == 64) e = csa::launch_attn<csa::bf16, 64, false>(p, s);
-    else e = csa::launch_attn<csa::bf16, 128, false>(p, s);
+    if (d == 16) e = csa::launch_attn16<16, false>(p, s);
+    else if (d == 64) e = csa::launch_attn16<64, false>(p, s);
+    else e = csa::launch_attn16<128, false>(p, s);
   }
   return e == hipSuccess ? CSA_OK : CSA_ERR_HIP;
 }

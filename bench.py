@@ -52,7 +52,7 @@ def _cpu_task(args):
     return int(np.sum(rows + 1))
 
 
-def cpu_baseline(w, q, k, v, k0, v0, heads=64, rows_per_head=32, seed=123):
+def cpu_baseline(w, q, k, v, k0, v0, heads=64, rows_per_head=320, seed=123):
     """Time the float64 reference on a seeded sample of (head, row) pairs.
 
     Runs before any GPU work (the pool forks).  Returns the cpu_baseline object.
@@ -89,6 +89,37 @@ def cpu_baseline(w, q, k, v, k0, v0, heads=64, rows_per_head=32, seed=123):
                    f"({len(tasks) * rows_per_head} of {total_rows} rows), float64 eq. (8), "
                    f"{workers} worker processes, {dt:.1f} s wall"),
     }
+
+
+# ------------------------------------------------------------------ HBM traffic
+
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn16_lm_B4H16T4096d128_hbm_traffic.txt")
+
+
+def measured_traffic(workload_name):
+    """HBM bytes per csa_forward launch from the committed rocprofv3 FETCH_SIZE/WRITE_SIZE
+    summary, or None when the workload differs or the kernel sources have changed since
+    the counters were taken (sha256 recorded in the summary)."""
+    import hashlib
+
+    if workload_name != "lm" or not os.path.exists(TRAFFIC_FILE):
+        return None
+    kv = {}
+    with open(TRAFFIC_FILE) as f:
+        for line in f:
+            if "=" in line and not line.lstrip().startswith("#"):
+                key, val = line.split("=", 1)
+                kv[key.strip()] = val.strip()
+    h = hashlib.sha256()
+    for rel in kv.get("kernel_sources", "").split():
+        path = os.path.join(ROOT, rel)
+        if not os.path.exists(path):
+            return None
+        with open(path, "rb") as f:
+            h.update(f.read())
+    if h.hexdigest() != kv.get("kernel_source_sha256"):
+        return None
+    return int(kv["csa_fetch_bytes"]) + int(kv["csa_write_bytes"])
 
 
 # ------------------------------------------------------------------ GPU leg
@@ -210,7 +241,7 @@ def main():
             "peak": peak,
             "unit": "TFLOP/s",
             "frac": round(tflops / peak, 4),
-            "traffic": None,
+            "traffic": measured_traffic(w.name),
         },
     }
     if not args.no_std:

@@ -24,3 +24,4 @@ from .csa import (  # noqa: F401
     std_row,
     std_reference,
 )
+from .first_order import csa1_reference, csa1_row  # noqa: F401

@@ -205,3 +205,58 @@ def dev_copied_sink(ref, seed=4):
     o, lse = ref(q, k, v, k0, v0, rows=[0])
     a1 = float(q[0, 0, 0] @ k[0, 0, 0])
     return max(float(np.abs(o[0, 0, 0] - v[0, 0, 0]).max()), abs(float(lse[0, 0, 0]) - a1))
+
+
+# ---------------------------------------------------------------- first-order variant
+
+def dev1_linear(ref, beta=0.7, T=6):
+    """First-order variant on linear logits a_i = beta i (k_0 = v_0 = 0, v_i = i c).
+
+    The second difference vanishes, so interior weights are e^{beta i}; the ends
+    carry e^{-ln 2 + x/3} with x = beta at i = 0 and x = -beta at i = t.  The sums
+    are taken in closed form (geometric and arithmetic-geometric series):
+    den = e^{beta/3}/2 + r (r^{t-1} - 1)/(r - 1) + e^{beta t - beta/3}/2,
+    num = c [ r (1 - t r^{t-1} + (t-1) r^t)/(1 - r)^2 + t e^{beta t - beta/3}/2 ],
+    r = e^beta.
+    """
+    d, dv = 3, 2
+    w = np.array([0.3, -0.2, 0.5])
+    qv = w * (beta / float(w @ w))
+    c = np.array([1.5, -0.25])
+    pos = np.arange(1, T + 1, dtype=np.float64)
+    q = np.broadcast_to(qv, (1, 1, T, d)).copy()
+    k = (pos[:, None] * w[None, :])[None, None]
+    v = (pos[:, None] * c[None, :])[None, None]
+    o, lse = ref(q, k, v, np.zeros((1, 1, d)), np.zeros((1, 1, dv)))
+    worst = 0.0
+    with mp.workdps(40):
+        bb = mp.mpf(beta)
+        r = mp.exp(bb)
+        for row in range(T):
+            t = row + 1
+            geo = r * (r ** (t - 1) - 1) / (r - 1) if t > 1 else mp.mpf(0)
+            ageo = r * (1 - t * r ** (t - 1) + (t - 1) * r ** t) / (1 - r) ** 2 if t > 1 else mp.mpf(0)
+            end_t = mp.exp(bb * t - bb / 3) / 2
+            den = mp.exp(bb / 3) / 2 + geo + end_t
+            ratio = (ageo + t * end_t) / den
+            o_exp = c * float(ratio)
+            l_exp = float(mp.log(den))
+            worst = max(worst, float(np.abs(o[0, 0, row] - o_exp).max()), abs(float(lse[0, 0, row]) - l_exp))
+    return worst
+
+
+def dev1_vs_exact(ref, eps, seed=3, t=6):
+    """max_i |b_i(first-order reference) - b_i(exact reference)| for logits of size eps.
+
+    eq. (13) is the first-order term of the exact b, so the gap is second order:
+    it must shrink like eps^2 (a wrong coefficient, sign or end constant leaves an
+    O(eps) or O(1) gap).
+    """
+    from oracle import csa_reference
+
+    rng = np.random.default_rng(seed)
+    q_t = rng.standard_normal(4) * eps
+    k_hat = rng.standard_normal((t + 1, 4))
+    b1, _ = implied_b(ref, q_t, k_hat, t)
+    b, _ = implied_b(csa_reference, q_t, k_hat, t)
+    return float(np.abs(b1 - b).max())

@@ -10,6 +10,7 @@ import inspect
 import pytest
 
 import oracle.csa as oracle_csa
+import oracle.first_order as oracle_first_order
 import pins
 
 MUTATIONS = {
@@ -37,12 +38,14 @@ CHECKS = [
 ]
 
 
-def _mutant(old, new):
-    src = inspect.getsource(oracle_csa)
+def _mutant(old, new, fn="csa_reference", module=oracle_csa):
+    src = inspect.getsource(module)
+    if module is not oracle_csa:  # the module imports a helper relatively
+        src = src.replace("from .csa import _as_f64", "from oracle.csa import _as_f64")
     assert src.count(old) == 1, f"mutation anchor not unique: {old!r}"
     ns = {"__name__": "oracle_mutant"}
     exec(compile(src.replace(old, new), "<oracle mutant>", "exec"), ns)
-    return ns["csa_reference"]
+    return ns[fn]
 
 
 def test_unmutated_reference_passes_every_check():
@@ -55,6 +58,43 @@ def test_mutant_is_caught(name):
     ref = _mutant(*MUTATIONS[name])
     caught = []
     for check, tol in CHECKS:
+        try:
+            caught.append(not (check(ref) < tol))
+        except Exception:
+            caught.append(True)
+    assert any(caught), f"mutation '{name}' escaped every pin"
+
+
+# ---------------------------------------------------------------- first-order variant
+
+MUTATIONS1 = {
+    "interior coefficient": ("- 2.0 * a[1:t]) / 6.0", "- 2.0 * a[1:t]) / 3.0"),
+    "interior own-logit weight": ("- 2.0 * a[1:t]) / 6.0", "- 1.0 * a[1:t]) / 6.0"),
+    "end slope sign at position 0": ("(a[1] - a[0]) / 3.0", "(a[0] - a[1]) / 3.0"),
+    "end slope sign at position t": ("(a[t - 1] - a[t]) / 3.0", "(a[t] - a[t - 1]) / 3.0"),
+    "end constant dropped": ("b[t] = -math.log(2.0) + ", "b[t] = 0.0 + "),
+    "values shifted by one position": ("o = (w @ V) / den", "o = (w @ np.roll(V, 1, axis=0)) / den"),
+    "lse without the shift": ("lse = shift + math.log(den)", "lse = math.log(den)"),
+}
+
+CHECKS1 = [
+    (pins.dev_trapezoid, 1e-13),
+    (pins.dev1_linear, 1e-11),
+    (lambda ref: pins.dev1_linear(ref, beta=-1.3), 1e-11),
+    (lambda ref: pins.dev1_vs_exact(ref, 0.01), 1e-3),
+]
+
+
+def test_unmutated_first_order_reference_passes_every_check():
+    for check, tol in CHECKS1:
+        assert check(oracle_first_order.csa1_reference) < tol
+
+
+@pytest.mark.parametrize("name", sorted(MUTATIONS1))
+def test_first_order_mutant_is_caught(name):
+    ref = _mutant(*MUTATIONS1[name], fn="csa1_reference", module=oracle_first_order)
+    caught = []
+    for check, tol in CHECKS1:
         try:
             caught.append(not (check(ref) < tol))
         except Exception:

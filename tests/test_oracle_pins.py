@@ -15,7 +15,7 @@ import numpy as np
 import pytest
 
 import pins
-from oracle import csa_reference, phi1, phi2, std_reference
+from oracle import csa1_reference, csa_reference, phi1, phi2, std_reference
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 
@@ -176,3 +176,33 @@ def test_golden_fixture():
         oq, lq = pins.quadrature_row(qq[r], kh, vh, r + 1)
         assert np.abs(np.array(g["o"])[0, 0, r] - oq).max() < 1e-12
         assert abs(g["lse"][0][0][r] - lq) < 1e-12
+
+
+# ---------------------------------------------------------------- first-order variant
+
+def test_first_order_trapezoid_for_equal_logits():
+    # equal logits: interior b = 0, ends -ln 2 -> the same 1/2, 1, ..., 1, 1/2 weights
+    assert pins.dev_trapezoid(csa1_reference) < 1e-13
+
+
+@pytest.mark.parametrize("beta", [0.7, -1.3, 2.5, 1e-3])
+def test_first_order_linear_logits_closed_form(beta):
+    assert pins.dev1_linear(csa1_reference, beta=beta) < 1e-11
+
+
+def test_first_order_agrees_with_exact_to_second_order():
+    devs = [pins.dev1_vs_exact(csa1_reference, eps) for eps in (0.08, 0.04, 0.02, 0.01)]
+    for big, small in zip(devs, devs[1:]):
+        assert 3.0 < big / small < 5.5, devs   # ~4: second order
+    assert devs[-1] < 1e-3
+
+
+def test_first_order_key_shift_invariance():
+    # k_i -> k_i + w for every position (k_0 included) adds q.w to every logit:
+    # b (a difference of logits) is unchanged, o is unchanged, lse moves by q.w
+    q, k, v, k0, v0 = pins.random_case(21, T=7)
+    w = np.array([0.4, -1.1, 0.25])
+    o, lse = csa1_reference(q, k, v, k0, v0)
+    o2, lse2 = csa1_reference(q, k + w, v, k0 + w, v0)
+    assert np.abs(o2 - o).max() < 1e-12
+    assert np.abs(lse2 - lse - (q @ w)).max() < 1e-12

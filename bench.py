@@ -8,7 +8,9 @@ Metric: TFLOP/s counting 4 T^2 d / 2 FLOP per (batch, head) -- QK^T plus PV
 over the causal half, the convention under which the pages call continuous
 and standard attention "essentially the same" in FLOPs -- and the fraction of
 the MI355X dense bf16 MFMA peak.  The standard-attention kernel built on the
-same tiling (std_fwd) runs on the same inputs for the ratio.
+same tiling (std_fwd) runs on the same inputs for the ratio, and so does the
+first-order variant (csa_forward_first_order, b as the second difference of the
+logits) -- the same kernel without the exact correction weights.
 
 Prints ONE JSON line.  `cpu_baseline` times the float64 CPU reference on a
 bounded sample of query rows of the same workload (process pool over host
@@ -166,6 +168,9 @@ def counters_mode(w, q, k, v, k0, v0):
     torch.cuda.synchronize()
     csa.std_fwd(qd, kd, vd)
     torch.cuda.synchronize()
+    if w.dtype == "bf16":
+        csa.csa_forward_first_order(qd, kd, vd, k0d, v0d)
+        torch.cuda.synchronize()
     print(json.dumps({"counters_run": w.name, "copy_bytes": 2 * src.numel() * 4}), flush=True)
 
 
@@ -177,6 +182,7 @@ def main():
     ap.add_argument("--workload", default="lm")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-std", action="store_true")
+    ap.add_argument("--no-first-order", action="store_true")
     ap.add_argument("--counters", action="store_true",
                     help="for rocprofv3 --pmc passes: one plain device copy of 256 MiB (counter "
                          "calibration), one csa_forward and one std_fwd launch, then exit")
@@ -256,6 +262,18 @@ def main():
         res["std_attention"] = {"value": round(s_tflops, 2), "unit": "TFLOP/s", "kernel_ms": round(s_avg, 4),
                                 "pct_peak": round(100.0 * s_tflops / peak, 2)}
         res["ratio_vs_std"] = round(tflops / s_tflops, 4)
+    if not args.no_first_order and w.dtype == "bf16":
+        fout = torch.empty_like(qd)
+        flse = torch.empty_like(lse)
+
+        def first_step():
+            csa.csa_forward_first_order(qd, kd, vd, k0d, v0d, out=fout, lse=flse, stream=stream)
+
+        f_avg, _, _ = time_kernel(first_step, args.steps, args.warmup, stream)
+        f_tflops = flop / (f_avg * 1e-3) / 1e12
+        res["first_order"] = {"value": round(f_tflops, 2), "unit": "TFLOP/s", "kernel_ms": round(f_avg, 4),
+                              "pct_peak": round(100.0 * f_tflops / peak, 2),
+                              "exact_over_first_order": round(tflops / f_tflops, 4)}
     if cpu is not None:
         res["cpu_baseline"] = cpu
     print(json.dumps(res), flush=True)

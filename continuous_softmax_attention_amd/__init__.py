@@ -20,6 +20,9 @@ from ._lib import (  # noqa: F401
     CsaError,
     csa_forward,
     csa_forward_check,
+    csa_forward_first_order,
+    csa_forward_first_order_check,
+    csa_forward_first_order_raw,
     csa_forward_raw,
     header_functions,
     library_path,

@@ -35,6 +35,8 @@ _i64 = ctypes.c_int64
 _SIGS = {
     "csa_forward": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, ctypes.c_int, _vp]),
     "csa_forward_check": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, ctypes.c_int]),
+    "csa_forward_first_order": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, ctypes.c_int, _vp]),
+    "csa_forward_first_order_check": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, ctypes.c_int]),
     "csa_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "std_fwd": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, ctypes.c_int, _vp]),
     "std_fwd_check": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, ctypes.c_int]),
@@ -88,12 +90,21 @@ def csa_forward_raw(q, k, v, k0, v0, out, lse, B, H, T, d, dtype, stream=0) -> i
     return load().csa_forward(q, k, v, k0 or None, v0 or None, out, lse or None, B, H, T, d, dtype, stream or None)
 
 
+def csa_forward_first_order_raw(q, k, v, k0, v0, out, lse, B, H, T, d, dtype, stream=0) -> int:
+    return load().csa_forward_first_order(q, k, v, k0 or None, v0 or None, out, lse or None, B, H, T, d, dtype,
+                                          stream or None)
+
+
 def std_fwd_raw(q, k, v, out, lse, B, H, T, d, dtype, stream=0) -> int:
     return load("libcsa_bench.so").std_fwd(q, k, v, out, lse or None, B, H, T, d, dtype, stream or None)
 
 
 def csa_forward_check(q, k, v, k0, v0, out, lse, B, H, T, d, dtype) -> int:
     return load().csa_forward_check(q, k, v, k0, v0, out, lse, B, H, T, d, dtype)
+
+
+def csa_forward_first_order_check(q, k, v, k0, v0, out, lse, B, H, T, d, dtype) -> int:
+    return load().csa_forward_first_order_check(q, k, v, k0, v0, out, lse, B, H, T, d, dtype)
 
 
 def std_fwd_check(q, k, v, out, lse, B, H, T, d, dtype) -> int:
@@ -138,6 +149,16 @@ def csa_forward(q, k, v, k0=None, v0=None, *, out=None, lse=None, return_lse=Tru
     k0, v0: [B, H, d] or None (zeros).  Returns (out, lse) -- lse is float32
     [B, H, T] (None when return_lse is False and no lse buffer is given).
     """
+    return _csa_call("csa_forward", q, k, v, k0, v0, out, lse, return_lse, stream)
+
+
+def csa_forward_first_order(q, k, v, k0=None, v0=None, *, out=None, lse=None, return_lse=True, stream=None):
+    """The first-order variant (b as the second difference of the logits, eq. (13)) through
+    libcsa; bfloat16 only.  Same arguments and results as csa_forward."""
+    return _csa_call("csa_forward_first_order", q, k, v, k0, v0, out, lse, return_lse, stream)
+
+
+def _csa_call(symbol, q, k, v, k0, v0, out, lse, return_lse, stream):
     import torch
 
     if q.dim() != 4:
@@ -146,7 +167,7 @@ def csa_forward(q, k, v, k0=None, v0=None, *, out=None, lse=None, return_lse=Tru
     dt = q.dtype
     dev = q.device
     if dev.type != "cuda":
-        raise ValueError("csa_forward runs on the GPU only; inputs must be device tensors")
+        raise ValueError(f"{symbol} runs on the GPU only; inputs must be device tensors")
     for name, t in (("q", q), ("k", k), ("v", v)):
         _check(name, t, (B, H, T, d), dt, dev)
     for name, t in (("k0", k0), ("v0", v0)):
@@ -160,13 +181,13 @@ def csa_forward(q, k, v, k0=None, v0=None, *, out=None, lse=None, return_lse=Tru
         lse = torch.empty((B, H, T), dtype=torch.float32, device=dev)
     elif lse is not None:
         _check("lse", lse, (B, H, T), torch.float32, dev)
-    st = load().csa_forward(
+    st = getattr(load(), symbol)(
         q.data_ptr(), k.data_ptr(), v.data_ptr(),
         k0.data_ptr() if k0 is not None else None, v0.data_ptr() if v0 is not None else None,
         out.data_ptr(), lse.data_ptr() if lse is not None else None,
         B, H, T, d, _dtype_code(q), _stream_handle(stream, dev))
     if st != CSA_OK:
-        raise CsaError(st, "csa_forward")
+        raise CsaError(st, symbol)
     return out, lse
 
 

@@ -1,8 +1,11 @@
-// bf16 causal attention forward for gfx950 on 16x16x32 MFMAs: continuous softmax
-// attention (CSA = true) and standard softmax attention on the identical tiling.
+// bf16 causal attention forward for gfx950 on 16x16x32 MFMAs, with three weight rules
+// on the identical tiling: continuous softmax attention (kExact), its first-order form
+// (kFirstOrder) and standard softmax attention (kSoftmax).
 //
 // Method: J. Su, "Continuous Softmax Attention", eq. (10)-(11) -- see attn_fwd.hpp
-// for the correction-weight arithmetic ("p-form"), which is shared.
+// for the correction-weight arithmetic ("p-form"), which is shared; the first-order
+// form replaces b by the second difference of the logits (Analysis of the Result,
+// eq. (13)).
 //
 // Why a second tiling.  With 32 queries per wave (32x32 MFMAs) the accumulator of
 // O^T alone takes 64 VGPRs and the kernel needs ~244, which caps the SIMD at two
@@ -53,6 +56,10 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kWaves16 = 8;  // 8 waves x 16 queries = 128 rows, as kBlockRows
 
+// Weight rule of a launch: standard softmax attention (eq. (12)), continuous softmax
+// attention (eq. (10)-(11)), or its first-order form with b expanded as in eq. (13).
+enum : int { kSoftmax = 0, kExact = 1, kFirstOrder = 2 };
+
 // One 16-byte HBM -> LDS copy per lane (global_load_lds_dwordx4): lane i reads
 // base + voff and writes LDS address lds_addr + 16 i (no instruction offset: it would
 // move the LDS destination as well).  Issued as inline asm so that the compiler does
@@ -90,9 +97,11 @@ __device__ __forceinline__ void edge_yu(float pl, float pr, float y, float u, fl
   L_right = small ? lt : lr;
 }
 
-template <int D, bool CSA>
+template <int D, int W>
 __global__ void __launch_bounds__(512, 4) attn16_kernel(FwdParams p) {
   static_assert(D == 16 || D == 64 || D == 128, "head dimension");
+  static_assert(W == kSoftmax || W == kExact || W == kFirstOrder, "weight rule");
+  constexpr bool CSA = W != kSoftmax;  // position 0, halo and neighbour terms
   constexpr int CH = D / 8;                      // 16-byte chunks per row
   constexpr int ROWB = D * 2;                    // bytes per row in HBM
   constexpr int NSTEP = D >= 32 ? D / 32 : 1;    // QK^T contraction steps (32 d each)
@@ -262,7 +271,8 @@ __global__ void __launch_bounds__(512, 4) attn16_kernel(FwdParams p) {
   for (int mb = 0; mb < NMB; ++mb) O[mb] = f32x4{};
   float lsum = 0.0f;     // this lane's share of the row sum of the rounded P
   float m_run = -__builtin_inff();
-  float carry = 0.0f;   // lanes g = 3: left term of the next tile's first key
+  float carry = 0.0f;   // lanes g = 3: left term of the next tile's first key (exact rule)
+  float carry_s = 0.0f; // logit of this lane's key 15 in the previous tile (first-order rule)
   float w0 = 0.0f;      // lanes g = 0: weight of position 0
 
   auto rescale_all = [&](float sc) {
@@ -375,6 +385,43 @@ __global__ void __launch_bounds__(512, 4) attn16_kernel(FwdParams p) {
       for (int t = 0; t < 16; ++t) {
         const float e = exp2_fast(alpha(t));
         w[t] = (!last || t <= lim) ? e : 0.0f;
+        slot(t);
+      }
+    } else if constexpr (W == kFirstOrder) {
+      // b to first order (eq. (13)); ends -ln 2 + x/3.  In base 2 with beta = alpha/6 an
+      // interior weight is 2^(4 beta_t + beta_{t-1} + beta_{t+1}) and an end weight
+      // 2^(4 beta_t + 2 beta_nb - 1); both exponents are averages of alphas covered by the
+      // running maximum, so the weights stay below 2^8.
+      const float c6 = kLog2e * (1.0f / 6.0f);
+      const float m6 = mr * (1.0f / 6.0f);
+      auto beta = [&](float logit) { return __builtin_fmaf(logit, c6, -m6); };
+      // neighbours as raw logits: left of key 0 is the previous group's key 15, or (g = 0)
+      // the previous tile's key 63 carried by lanes g = 3, or (first tile) position 0;
+      // right of key 15 is the next group's key 0, or (g = 3) the halo
+      const float lsend = g == 3 ? carry_s : s[15];
+      float left = from_lane(lane_up, lsend);
+      float right = from_lane(lane_dn, s[0]);
+      carry_s = s[15];
+      if (first && g == 0) left = a0;
+      if (!last && g == 3) right = halo;
+      if (first)  // position 0 has only its right neighbour, the first key (lanes g = 0)
+        w0 = exp2_fast(__builtin_fmaf(4.0f, beta(a0), __builtin_fmaf(2.0f, beta(s[0]), -1.0f)));
+      float bl = beta(left);
+      float bc = beta(s[0]);
+#pragma unroll
+      for (int t = 0; t < 16; ++t) {
+        const float bn = t < 15 ? beta(s[t + 1]) : beta(right);
+        float wv;
+        if constexpr (!last) {
+          wv = exp2_fast(__builtin_fmaf(4.0f, bc, bl + bn));
+        } else {  // diagonal tile: column t takes the end rule, columns > t get 0
+          const float wi = exp2_fast(__builtin_fmaf(4.0f, bc, bl + bn));
+          const float we = exp2_fast(__builtin_fmaf(4.0f, bc, __builtin_fmaf(2.0f, bl, -1.0f)));
+          wv = t < lim ? wi : (t == lim ? we : 0.0f);
+        }
+        w[t] = wv;
+        bl = bc;
+        bc = bn;
         slot(t);
       }
     } else {
@@ -534,19 +581,19 @@ __global__ void __launch_bounds__(512, 4) attn16_kernel(FwdParams p) {
       *(bf16x4*)(Og + d0) = bf16x4{(bf16)o4[0], (bf16)o4[1], (bf16)o4[2], (bf16)o4[3]};
     }
     if (p.lse != nullptr && g == 0) {
-      const float corr = CSA ? 0.7330258411633287f : 0.0f;  // -2 ln(ln 2)
+      const float corr = W == kExact ? 0.7330258411633287f : 0.0f;  // -2 ln(ln 2)
       p.lse[(size_t)bh * Tn + qr] = (m_run + __builtin_amdgcn_logf(l)) * kLn2 + corr;
     }
   }
 }
 
-template <int D, bool CSA>
+template <int D, int W>
 inline hipError_t launch_attn16(const FwdParams& prm, hipStream_t stream) {
   const int nqb = (prm.T + kBlockRows - 1) / kBlockRows;
   FwdParams p = prm;
   p.nqb = nqb;
   const dim3 grid((unsigned)(nqb * prm.B * prm.H));
-  hipLaunchKernelGGL((attn16_kernel<D, CSA>), grid, dim3(64 * kWaves16), 0, stream, p);
+  hipLaunchKernelGGL((attn16_kernel<D, W>), grid, dim3(64 * kWaves16), 0, stream, p);
   return hipGetLastError();
 }
 

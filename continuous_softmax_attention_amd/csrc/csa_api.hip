@@ -8,19 +8,34 @@
 
 namespace {
 
-template <bool CSA>
-int dispatch(const csa::FwdParams& p, int64_t d, int dtype, hipStream_t s) {
+int dispatch_exact(const csa::FwdParams& p, int64_t d, int dtype, hipStream_t s) {
   hipError_t e = hipErrorInvalidValue;
   if (dtype == CSA_F32) {
-    if (d == 16) e = csa::launch_attn<float, 16, CSA>(p, s);
-    else if (d == 64) e = csa::launch_attn<float, 64, CSA>(p, s);
-    else e = csa::launch_attn<float, 128, CSA>(p, s);
+    if (d == 16) e = csa::launch_attn<float, 16, true>(p, s);
+    else if (d == 64) e = csa::launch_attn<float, 64, true>(p, s);
+    else e = csa::launch_attn<float, 128, true>(p, s);
   } else {
-    if (d == 16) e = csa::launch_attn16<16, CSA>(p, s);
-    else if (d == 64) e = csa::launch_attn16<64, CSA>(p, s);
-    else e = csa::launch_attn16<128, CSA>(p, s);
+    if (d == 16) e = csa::launch_attn16<16, csa::kExact>(p, s);
+    else if (d == 64) e = csa::launch_attn16<64, csa::kExact>(p, s);
+    else e = csa::launch_attn16<128, csa::kExact>(p, s);
   }
   return e == hipSuccess ? CSA_OK : CSA_ERR_HIP;
+}
+
+int dispatch_first_order(const csa::FwdParams& p, int64_t d, hipStream_t s) {
+  hipError_t e = hipErrorInvalidValue;
+  if (d == 16) e = csa::launch_attn16<16, csa::kFirstOrder>(p, s);
+  else if (d == 64) e = csa::launch_attn16<64, csa::kFirstOrder>(p, s);
+  else e = csa::launch_attn16<128, csa::kFirstOrder>(p, s);
+  return e == hipSuccess ? CSA_OK : CSA_ERR_HIP;
+}
+
+int validate_first_order(const void* q, const void* k, const void* v, const void* k0,
+                         const void* v0, const void* out, const float* lse, int64_t B,
+                         int64_t H, int64_t T, int64_t d, int dtype) {
+  const int st = csa::validate(q, k, v, k0, v0, out, lse, B, H, T, d, dtype, true);
+  if (st != CSA_OK) return st;
+  return dtype == CSA_BF16 ? CSA_OK : CSA_ERR_UNSUPPORTED;  // bf16 kernel only
 }
 
 }  // namespace
@@ -37,7 +52,24 @@ extern "C" int csa_forward(const void* q, const void* k, const void* v, const vo
   const int st = csa::validate(q, k, v, k0, v0, out, lse, B, H, T, d, dtype, true);
   if (st != CSA_OK) return st;
   csa::FwdParams p{q, k, v, k0, v0, out, lse, (int)B, (int)H, (int)T, 0};
-  return dispatch<true>(p, d, dtype, (hipStream_t)stream);
+  return dispatch_exact(p, d, dtype, (hipStream_t)stream);
+}
+
+extern "C" int csa_forward_first_order_check(const void* q, const void* k, const void* v,
+                                             const void* k0, const void* v0, const void* out,
+                                             const float* lse, int64_t B, int64_t H, int64_t T,
+                                             int64_t d, int dtype) {
+  return validate_first_order(q, k, v, k0, v0, out, lse, B, H, T, d, dtype);
+}
+
+extern "C" int csa_forward_first_order(const void* q, const void* k, const void* v,
+                                       const void* k0, const void* v0, void* out, float* lse,
+                                       int64_t B, int64_t H, int64_t T, int64_t d, int dtype,
+                                       void* stream) {
+  const int st = validate_first_order(q, k, v, k0, v0, out, lse, B, H, T, d, dtype);
+  if (st != CSA_OK) return st;
+  csa::FwdParams p{q, k, v, k0, v0, out, lse, (int)B, (int)H, (int)T, 0};
+  return dispatch_first_order(p, d, (hipStream_t)stream);
 }
 
 extern "C" const char* csa_status_string(int status) { return csa::status_string(status); }

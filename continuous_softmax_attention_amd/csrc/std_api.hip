@@ -24,9 +24,9 @@ extern "C" int std_fwd(const void* q, const void* k, const void* v, void* out, f
     else if (d == 64) e = csa::launch_attn<float, 64, false>(p, s);
     else e = csa::launch_attn<float, 128, false>(p, s);
   } else {
-    if (d == 16) e = csa::launch_attn16<16, false>(p, s);
-    else if (d == 64) e = csa::launch_attn16<64, false>(p, s);
-    else e = csa::launch_attn16<128, false>(p, s);
+    if (d == 16) e = csa::launch_attn16<16, csa::kSoftmax>(p, s);
+    else if (d == 64) e = csa::launch_attn16<64, csa::kSoftmax>(p, s);
+    else e = csa::launch_attn16<128, csa::kSoftmax>(p, s);
   }
   return e == hipSuccess ? CSA_OK : CSA_ERR_HIP;
 }

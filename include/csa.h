@@ -47,7 +47,7 @@ typedef enum {
 enum {
   CSA_OK = 0,
   CSA_ERR_INVALID_ARG = 1, /* NULL pointer, non-positive size, misaligned or overlapping buffer, size overflow */
-  CSA_ERR_UNSUPPORTED = 2, /* head dimension d not in {16, 64, 128}, or unknown dtype */
+  CSA_ERR_UNSUPPORTED = 2, /* head dimension d not in {16, 64, 128}, or a dtype the entry point does not take */
   CSA_ERR_HIP = 3          /* the kernel launch was rejected by the HIP runtime */
 };
 
@@ -85,6 +85,30 @@ int csa_forward(const void* q, const void* k, const void* v, const void* k0, con
 int csa_forward_check(const void* q, const void* k, const void* v, const void* k0, const void* v0,
                       const void* out, const float* lse, int64_t B, int64_t H, int64_t T, int64_t d,
                       int dtype);
+
+/*
+ * csa_forward_first_order -- the same forward with b replaced by its first-order
+ * expansion (Analysis of the Result, eq. (13)): for 1 <= i <= t-1
+ *
+ *     b_{t,i} = (a_{t,i-1} + a_{t,i+1} - 2 a_{t,i}) / 6,
+ *
+ * the second difference of the logits (the "short convolution" reading of the
+ * method), and at the two end positions, which keep a single phi_2 term in
+ * eq. (10), b = -ln 2 + x/3 with x = a_{t,1} - a_{t,0} at i = 0 and
+ * x = a_{t,t-1} - a_{t,t} at i = t (phi_2(x) = 1/2 + x/6 + ... expanded the same
+ * way).  o_t is eq. (11) with these b; lse_t = ln sum_i e^{a_{t,i} + b_{t,i}}.
+ *
+ * Arguments, layouts, ownership and return codes as csa_forward, except that
+ * dtype must be CSA_BF16 (CSA_F32 returns CSA_ERR_UNSUPPORTED).
+ */
+int csa_forward_first_order(const void* q, const void* k, const void* v, const void* k0,
+                            const void* v0, void* out, float* lse, int64_t B, int64_t H, int64_t T,
+                            int64_t d, int dtype, void* stream);
+
+/* The argument validation of csa_forward_first_order alone (no HIP call). */
+int csa_forward_first_order_check(const void* q, const void* k, const void* v, const void* k0,
+                                  const void* v0, const void* out, const float* lse, int64_t B,
+                                  int64_t H, int64_t T, int64_t d, int dtype);
 
 /* Static, NUL-terminated description of a return code. */
 const char* csa_status_string(int status);

@@ -34,7 +34,8 @@ def test_exports_every_declared_symbol(lib, header):
 
 
 def test_header_declares_the_entry_points():
-    assert {"csa_forward", "csa_forward_check", "csa_status_string"} <= set(csa.header_functions("csa.h"))
+    assert {"csa_forward", "csa_forward_check", "csa_forward_first_order", "csa_forward_first_order_check",
+            "csa_status_string"} <= set(csa.header_functions("csa.h"))
     assert {"std_fwd", "std_fwd_check"} <= set(csa.header_functions("csa_bench.h"))
 
 
@@ -114,6 +115,30 @@ def test_std_check_matches_rules():
     assert csa.std_fwd_check(A, A + MB, A + 2 * MB, A + 3 * MB, None, 1, 2, 64, 128, csa.CSA_BF16) == OK
     assert csa.std_fwd_check(A, A + MB, A + 2 * MB, A + MB, None, 1, 2, 64, 128, csa.CSA_BF16) == INV
     assert csa.std_fwd_check(A, A + MB, A + 2 * MB, A + 3 * MB, None, 1, 2, 64, 100, csa.CSA_BF16) == UNS
+
+
+def _check1(**kw):
+    a = _args(**kw)
+    return csa.csa_forward_first_order_check(a["q"], a["k"], a["v"], a["k0"], a["v0"], a["out"], a["lse"],
+                                             a["B"], a["H"], a["T"], a["d"], a["dtype"])
+
+
+def test_first_order_check_rules():
+    # same validation as csa_forward, and bf16 only
+    assert _check1() == OK
+    assert _check1(k0=A + 300 * MB, v0=A + 301 * MB, lse=None) == OK
+    for d in (16, 64, 128):
+        assert _check1(d=d) == OK
+        assert _check1(d=d, dtype=csa.CSA_F32) == UNS
+    assert _check1(d=96) == UNS
+    assert _check1(q=None) == INV
+    assert _check1(T=0) == INV
+    assert _check1(out=A + 64 * MB + 4096) == INV
+    assert _check1(k0=A + 300 * MB + 8) == INV
+    # the launching entry point rejects the same calls before any HIP call
+    assert csa.csa_forward_first_order_raw(None, A, A, None, None, A + MB, None, 1, 1, 8, 64, csa.CSA_BF16) == INV
+    assert csa.csa_forward_first_order_raw(A, A + MB, A + 2 * MB, None, None, A + 3 * MB, None, 1, 1, 8, 64,
+                                           csa.CSA_F32) == UNS
 
 
 def test_status_strings():

@@ -10,7 +10,9 @@ and standard attention "essentially the same" in FLOPs -- and the fraction of
 the MI355X dense bf16 MFMA peak.  The standard-attention kernel built on the
 same tiling (std_fwd) runs on the same inputs for the ratio, and so does the
 first-order variant (csa_forward_first_order, b as the second difference of the
-logits) -- the same kernel without the exact correction weights.
+logits) -- the same kernel without the exact correction weights.  The ``decode``
+object times csa_decode (a few new queries against a key/value cache, bound by HBM
+bandwidth) on the decode workloads.
 
 Prints ONE JSON line.  `cpu_baseline` times the float64 CPU reference on a
 bounded sample of query rows of the same workload (process pool over host
@@ -148,6 +150,39 @@ def time_kernel(fn, steps, warmup, stream):
     return sum(per) / len(per), min(per), wall_ms
 
 
+def decode_legs(steps, warmup):
+    """csa_decode on the decode workloads: HBM bandwidth of the whole call (both launches),
+    counting the key/value cache read once (the algorithmic bytes; q, out and lse are
+    under 0.1% of them)."""
+    import torch
+
+    import continuous_softmax_attention_amd as csa
+    from workloads import DECODE_WORKLOADS, make_decode_inputs
+
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream(dev)
+    legs = {}
+    for name, w in DECODE_WORKLOADS.items():
+        q, k, v, k0, v0 = make_decode_inputs(w)
+        qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
+        del q, k, v
+        out = torch.empty_like(qd)
+        lse = torch.empty((w.B, w.H, w.Tq), dtype=torch.float32, device=dev)
+        ws = torch.empty(csa.csa_decode_workspace_bytes(w.B, w.H, w.Tq, w.T, w.d), dtype=torch.uint8, device=dev)
+
+        def step():
+            csa.csa_decode(qd, kd, vd, None, None, out=out, lse=lse, workspace=ws, stream=stream)
+
+        avg_ms, min_ms, _ = time_kernel(step, steps, warmup, stream)
+        gbs = w.cache_bytes / (avg_ms * 1e-3) / 1e9
+        legs[name] = {"workload": f"B{w.B} H{w.H} Tq{w.Tq} T{w.T} d{w.d} {w.dtype}", "value": round(gbs, 1),
+                      "unit": "GB/s", "ms": round(avg_ms, 4), "min_ms": round(min_ms, 4),
+                      "bytes": w.cache_bytes, "frac_hbm": round(gbs / PEAK_HBM_GBS, 4)}
+        del qd, kd, vd, out, lse, ws
+        torch.cuda.empty_cache()
+    return legs
+
+
 def counters_mode(w, q, k, v, k0, v0):
     """One launch of each kernel plus a 256 MiB device-to-device copy whose HBM bytes
     are known (256 MiB read + 256 MiB written), to scale FETCH_SIZE/WRITE_SIZE."""
@@ -183,6 +218,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-std", action="store_true")
     ap.add_argument("--no-first-order", action="store_true")
+    ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--counters", action="store_true",
                     help="for rocprofv3 --pmc passes: one plain device copy of 256 MiB (counter "
                          "calibration), one csa_forward and one std_fwd launch, then exit")
@@ -274,6 +310,8 @@ def main():
         res["first_order"] = {"value": round(f_tflops, 2), "unit": "TFLOP/s", "kernel_ms": round(f_avg, 4),
                               "pct_peak": round(100.0 * f_tflops / peak, 2),
                               "exact_over_first_order": round(tflops / f_tflops, 4)}
+    if not args.no_decode:
+        res["decode"] = decode_legs(args.steps, args.warmup)
     if cpu is not None:
         res["cpu_baseline"] = cpu
     print(json.dumps(res), flush=True)

@@ -18,6 +18,10 @@ from ._lib import (  # noqa: F401
     CSA_F32,
     CSA_OK,
     CsaError,
+    csa_decode,
+    csa_decode_check,
+    csa_decode_raw,
+    csa_decode_workspace_bytes,
     csa_forward,
     csa_forward_check,
     csa_forward_first_order,

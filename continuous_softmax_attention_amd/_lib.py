@@ -37,6 +37,11 @@ _SIGS = {
     "csa_forward_check": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, ctypes.c_int]),
     "csa_forward_first_order": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, ctypes.c_int, _vp]),
     "csa_forward_first_order_check": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, ctypes.c_int]),
+    "csa_decode": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64, _i64,
+                                  ctypes.c_int, _vp]),
+    "csa_decode_check": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64, _i64,
+                                        ctypes.c_int]),
+    "csa_decode_workspace_bytes": (_i64, [_i64, _i64, _i64, _i64, _i64]),
     "csa_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "std_fwd": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, ctypes.c_int, _vp]),
     "std_fwd_check": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, ctypes.c_int]),
@@ -93,6 +98,20 @@ def csa_forward_raw(q, k, v, k0, v0, out, lse, B, H, T, d, dtype, stream=0) -> i
 def csa_forward_first_order_raw(q, k, v, k0, v0, out, lse, B, H, T, d, dtype, stream=0) -> int:
     return load().csa_forward_first_order(q, k, v, k0 or None, v0 or None, out, lse or None, B, H, T, d, dtype,
                                           stream or None)
+
+
+def csa_decode_raw(q, k, v, k0, v0, out, lse, ws, ws_bytes, B, H, Tq, T, d, dtype, stream=0) -> int:
+    return load().csa_decode(q, k, v, k0 or None, v0 or None, out, lse or None, ws, ws_bytes, B, H, Tq, T, d, dtype,
+                             stream or None)
+
+
+def csa_decode_check(q, k, v, k0, v0, out, lse, ws, ws_bytes, B, H, Tq, T, d, dtype) -> int:
+    return load().csa_decode_check(q, k, v, k0, v0, out, lse, ws, ws_bytes, B, H, Tq, T, d, dtype)
+
+
+def csa_decode_workspace_bytes(B, H, Tq, T, d) -> int:
+    """Bytes of workspace csa_decode needs (-1 for invalid sizes)."""
+    return int(load().csa_decode_workspace_bytes(B, H, Tq, T, d))
 
 
 def std_fwd_raw(q, k, v, out, lse, B, H, T, d, dtype, stream=0) -> int:
@@ -214,4 +233,51 @@ def std_fwd(q, k, v, *, out=None, lse=None, return_lse=True, stream=None):
         lse.data_ptr() if lse is not None else None, B, H, T, d, _dtype_code(q), _stream_handle(stream, dev))
     if st != CSA_OK:
         raise CsaError(st, "std_fwd")
+    return out, lse
+
+
+def csa_decode(q, k, v, k0=None, v0=None, *, out=None, lse=None, return_lse=True, workspace=None, stream=None):
+    """Forward of a few new queries against a key/value cache through libcsa.
+
+    q: [B, H, Tq, d] (the queries at positions T-Tq+1..T, 1 <= Tq <= 8); k, v: [B, H, T, d];
+    k0, v0: [B, H, d] or None.  ``workspace`` is a device tensor of at least
+    csa_decode_workspace_bytes(B, H, Tq, T, d) bytes (allocated here when None).
+    Returns (out [B, H, Tq, d], lse [B, H, Tq] float32 or None).
+    """
+    import torch
+
+    if q.dim() != 4 or k.dim() != 4:
+        raise ValueError("q must be [B, H, Tq, d] and k, v [B, H, T, d]")
+    B, H, Tq, d = q.shape
+    T = k.shape[2]
+    dt, dev = q.dtype, q.device
+    if dev.type != "cuda":
+        raise ValueError("csa_decode runs on the GPU only; inputs must be device tensors")
+    _check("q", q, (B, H, Tq, d), dt, dev)
+    for name, t in (("k", k), ("v", v)):
+        _check(name, t, (B, H, T, d), dt, dev)
+    for name, t in (("k0", k0), ("v0", v0)):
+        if t is not None:
+            _check(name, t, (B, H, d), dt, dev)
+    need = csa_decode_workspace_bytes(B, H, Tq, T, d)
+    if need < 0:
+        raise CsaError(CSA_ERR_INVALID_ARG, "csa_decode (sizes)")
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    if out is None:
+        out = torch.empty_like(q)
+    else:
+        _check("out", out, (B, H, Tq, d), dt, dev)
+    if lse is None and return_lse:
+        lse = torch.empty((B, H, Tq), dtype=torch.float32, device=dev)
+    elif lse is not None:
+        _check("lse", lse, (B, H, Tq), torch.float32, dev)
+    st = load().csa_decode(
+        q.data_ptr(), k.data_ptr(), v.data_ptr(),
+        k0.data_ptr() if k0 is not None else None, v0.data_ptr() if v0 is not None else None,
+        out.data_ptr(), lse.data_ptr() if lse is not None else None,
+        workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+        B, H, Tq, T, d, _dtype_code(q), _stream_handle(stream, dev))
+    if st != CSA_OK:
+        raise CsaError(st, "csa_decode")
     return out, lse

@@ -2,6 +2,7 @@
 #include <hip/hip_runtime.h>
 
 #include "attn16.hpp"
+#include "decode.hpp"
 #include "attn_fwd.hpp"
 #include "csa.h"
 #include "validate.hpp"
@@ -73,3 +74,36 @@ extern "C" int csa_forward_first_order(const void* q, const void* k, const void*
 }
 
 extern "C" const char* csa_status_string(int status) { return csa::status_string(status); }
+
+extern "C" int64_t csa_decode_workspace_bytes(int64_t B, int64_t H, int64_t Tq, int64_t T, int64_t d) {
+  return csa::decode_workspace_bytes(B, H, Tq, T, d);
+}
+
+extern "C" int csa_decode_check(const void* q, const void* k, const void* v, const void* k0, const void* v0,
+                                const void* out, const float* lse, const void* workspace,
+                                int64_t workspace_bytes, int64_t B, int64_t H, int64_t Tq, int64_t T,
+                                int64_t d, int dtype) {
+  return csa::validate_decode(q, k, v, k0, v0, out, lse, workspace, workspace_bytes, B, H, Tq, T, d, dtype);
+}
+
+extern "C" int csa_decode(const void* q, const void* k, const void* v, const void* k0, const void* v0,
+                          void* out, float* lse, void* workspace, int64_t workspace_bytes, int64_t B,
+                          int64_t H, int64_t Tq, int64_t T, int64_t d, int dtype, void* stream) {
+  const int st =
+      csa::validate_decode(q, k, v, k0, v0, out, lse, workspace, workspace_bytes, B, H, Tq, T, d, dtype);
+  if (st != CSA_OK) return st;
+  csa::DecParams p{q, k, v, k0, v0, out, lse, (float*)workspace,
+                   (int)(B * H), (int)Tq, (int)T, csa::decode_splits(T)};
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e = hipErrorInvalidValue;
+  if (dtype == CSA_F32) {
+    if (d == 16) e = csa::launch_decode<float, 16>(p, s);
+    else if (d == 64) e = csa::launch_decode<float, 64>(p, s);
+    else e = csa::launch_decode<float, 128>(p, s);
+  } else {
+    if (d == 16) e = csa::launch_decode<csa::bf16, 16>(p, s);
+    else if (d == 64) e = csa::launch_decode<csa::bf16, 64>(p, s);
+    else e = csa::launch_decode<csa::bf16, 128>(p, s);
+  }
+  return e == hipSuccess ? CSA_OK : CSA_ERR_HIP;
+}

@@ -60,6 +60,43 @@ inline int validate(const void* q, const void* k, const void* v, const void* k0,
   return CSA_OK;
 }
 
+// Checks of the decode entry points (csa_forward's rules for the shared arguments, plus
+// 1 <= Tq <= 8, Tq <= T, and a workspace large enough and disjoint from everything).
+inline int64_t decode_workspace_bytes(int64_t B, int64_t H, int64_t Tq, int64_t T, int64_t d) {
+  if (B < 1 || H < 1 || T < 1 || Tq < 1 || Tq > 8 || Tq > T) return -1;
+  if (d != 16 && d != 64 && d != 128) return -1;
+  const int64_t kMax32 = (int64_t(1) << 31) - 1;
+  if (T > kMax32 / 2 || B > kMax32 || H > kMax32 || B * H > kMax32) return -1;
+  const int64_t nsplit = (T + 1 + 511) / 512;
+  if (B * H > kMax32 / nsplit) return -1;
+  return B * H * nsplit * Tq * (d + 2) * 4;
+}
+
+inline int validate_decode(const void* q, const void* k, const void* v, const void* k0, const void* v0,
+                           const void* out, const float* lse, const void* ws, int64_t ws_bytes, int64_t B,
+                           int64_t H, int64_t Tq, int64_t T, int64_t d, int dtype) {
+  if (dtype != CSA_F32 && dtype != CSA_BF16) return CSA_ERR_UNSUPPORTED;
+  if (d != 16 && d != 64 && d != 128) return CSA_ERR_UNSUPPORTED;
+  if (!q || !k || !v || !out || !ws) return CSA_ERR_INVALID_ARG;
+  const int64_t need = decode_workspace_bytes(B, H, Tq, T, d);
+  if (need < 0 || ws_bytes < need) return CSA_ERR_INVALID_ARG;
+  const int64_t esize = dtype == CSA_F32 ? 4 : 2;
+  if (B * H > INT64_MAX / (T * d * esize)) return CSA_ERR_INVALID_ARG;
+  for (const void* p : {q, k, v, out, ws})
+    if (!aligned(p, 16)) return CSA_ERR_INVALID_ARG;
+  if (k0 && !aligned(k0, 16)) return CSA_ERR_INVALID_ARG;
+  if (v0 && !aligned(v0, 16)) return CSA_ERR_INVALID_ARG;
+  if (lse && !aligned(lse, 4)) return CSA_ERR_INVALID_ARG;
+  const int64_t cache = B * H * T * d * esize, qbytes = B * H * Tq * d * esize;
+  const Span so = span_of(out, qbytes), sl = span_of(lse, B * H * Tq * 4), sw = span_of(ws, need);
+  const Span ins[5] = {span_of(q, qbytes), span_of(k, cache), span_of(v, cache),
+                       span_of(k0, B * H * d * esize), span_of(v0, B * H * d * esize)};
+  for (const Span& s : ins)
+    if (overlaps(so, s) || overlaps(sl, s) || overlaps(sw, s)) return CSA_ERR_INVALID_ARG;
+  if (overlaps(so, sl) || overlaps(so, sw) || overlaps(sl, sw)) return CSA_ERR_INVALID_ARG;
+  return CSA_OK;
+}
+
 inline const char* status_string(int s) {
   switch (s) {
     case CSA_OK: return "ok";

@@ -110,6 +110,40 @@ int csa_forward_first_order_check(const void* q, const void* k, const void* v, c
                                   const void* v0, const void* out, const float* lse, int64_t B,
                                   int64_t H, int64_t T, int64_t d, int dtype);
 
+/*
+ * csa_decode -- the forward for a few new queries against a key/value cache (decoding
+ * or speculative verification): the Tq queries are the last positions T-Tq+1..T of a
+ * sequence whose keys/values at positions 1..T (and k_0, v_0 at position 0) are in the
+ * cache.  Query j (0-based) is position t_j = T - Tq + 1 + j and sees positions 0..t_j;
+ * o and lse are exactly those rows of csa_forward (eq. (10)-(11)).
+ *
+ *   q          device, [B, H, Tq, d] contiguous, `dtype`, 16-byte aligned; 1 <= Tq <= 8, Tq <= T.
+ *   k, v       device, [B, H, T, d] contiguous cache, `dtype`, 16-byte aligned.
+ *   k0, v0     as in csa_forward (NULL = zeros).
+ *   out        device, [B, H, Tq, d], `dtype`, 16-byte aligned.
+ *   lse        device, [B, H, Tq] float32, 4-byte aligned, or NULL.
+ *   workspace  device, 16-byte aligned, at least csa_decode_workspace_bytes(B, H, Tq, T, d)
+ *              bytes, owned by the caller and used for per-split partial results; its
+ *              contents need no initialisation and are scratch after the call.  Calls that
+ *              share a workspace must be ordered on one stream.
+ *   Other arguments and return codes as csa_forward (CSA_ERR_INVALID_ARG also for Tq out
+ *   of range, a short or missing workspace, or any overlap among out, lse, workspace and
+ *   the inputs).
+ *
+ * Two kernel launches on `stream`: per-split partials, then their merge.
+ */
+int csa_decode(const void* q, const void* k, const void* v, const void* k0, const void* v0,
+               void* out, float* lse, void* workspace, int64_t workspace_bytes, int64_t B, int64_t H,
+               int64_t Tq, int64_t T, int64_t d, int dtype, void* stream);
+
+/* The argument validation of csa_decode alone (no HIP call). */
+int csa_decode_check(const void* q, const void* k, const void* v, const void* k0, const void* v0,
+                     const void* out, const float* lse, const void* workspace, int64_t workspace_bytes,
+                     int64_t B, int64_t H, int64_t Tq, int64_t T, int64_t d, int dtype);
+
+/* Workspace bytes csa_decode needs for these sizes, or -1 if the sizes are invalid. */
+int64_t csa_decode_workspace_bytes(int64_t B, int64_t H, int64_t Tq, int64_t T, int64_t d);
+
 /* Static, NUL-terminated description of a return code. */
 const char* csa_status_string(int status);
 

@@ -35,6 +35,7 @@ def test_exports_every_declared_symbol(lib, header):
 
 def test_header_declares_the_entry_points():
     assert {"csa_forward", "csa_forward_check", "csa_forward_first_order", "csa_forward_first_order_check",
+            "csa_decode", "csa_decode_check", "csa_decode_workspace_bytes",
             "csa_status_string"} <= set(csa.header_functions("csa.h"))
     assert {"std_fwd", "std_fwd_check"} <= set(csa.header_functions("csa_bench.h"))
 
@@ -139,6 +140,53 @@ def test_first_order_check_rules():
     assert csa.csa_forward_first_order_raw(None, A, A, None, None, A + MB, None, 1, 1, 8, 64, csa.CSA_BF16) == INV
     assert csa.csa_forward_first_order_raw(A, A + MB, A + 2 * MB, None, None, A + 3 * MB, None, 1, 1, 8, 64,
                                            csa.CSA_F32) == UNS
+
+
+def _dargs(**kw):
+    a = dict(q=A, k=A + 64 * MB, v=A + 128 * MB, k0=None, v0=None, out=A + 192 * MB, lse=A + 193 * MB,
+             ws=A + 256 * MB, wsb=None, B=2, H=3, Tq=4, T=1000, d=128, dtype=csa.CSA_BF16)
+    a.update(kw)
+    if a["wsb"] is None:
+        a["wsb"] = max(0, csa.csa_decode_workspace_bytes(a["B"], a["H"], a["Tq"], a["T"], a["d"]))
+    return a
+
+
+def _dcheck(**kw):
+    a = _dargs(**kw)
+    return csa.csa_decode_check(a["q"], a["k"], a["v"], a["k0"], a["v0"], a["out"], a["lse"], a["ws"], a["wsb"],
+                                a["B"], a["H"], a["Tq"], a["T"], a["d"], a["dtype"])
+
+
+def test_decode_workspace_size():
+    # one (O[d], m, l) float32 record per (head, split of 512 positions, query)
+    assert csa.csa_decode_workspace_bytes(2, 3, 4, 1000, 128) == 2 * 3 * 2 * 4 * 130 * 4
+    assert csa.csa_decode_workspace_bytes(1, 1, 1, 511, 64) == 1 * 1 * 1 * 1 * 66 * 4
+    assert csa.csa_decode_workspace_bytes(1, 1, 1, 512, 64) == 2 * 66 * 4
+    for bad in (dict(Tq=0), dict(Tq=9), dict(Tq=5, T=4), dict(d=32), dict(B=0), dict(T=0)):
+        a = dict(B=1, H=1, Tq=1, T=100, d=64)
+        a.update(bad)
+        assert csa.csa_decode_workspace_bytes(a["B"], a["H"], a["Tq"], a["T"], a["d"]) == -1
+
+
+def test_decode_check_rules():
+    assert _dcheck() == OK
+    assert _dcheck(k0=A + 300 * MB, v0=A + 301 * MB, lse=None) == OK
+    assert _dcheck(Tq=1, T=1) == OK
+    for d in (16, 64, 128):
+        for dt in (csa.CSA_F32, csa.CSA_BF16):
+            assert _dcheck(d=d, dtype=dt) == OK
+    assert _dcheck(d=96) == UNS
+    assert _dcheck(dtype=5) == UNS
+    for bad in (dict(Tq=0), dict(Tq=9), dict(Tq=8, T=7), dict(ws=None), dict(wsb=16), dict(q=None),
+                dict(ws=A + 256 * MB + 8), dict(out=A + 192 * MB + 2), dict(lse=A + 193 * MB + 2),
+                dict(ws=A + 64 * MB + 4096),                    # workspace inside k
+                dict(out=A + 256 * MB + 64),                    # out inside the workspace
+                dict(lse=A + 192 * MB + 16)):                   # lse inside out
+        assert _dcheck(**bad) == INV, bad
+    # the launching entry point rejects the same calls before any HIP call
+    a = _dargs(Tq=9)
+    assert csa.csa_decode_raw(a["q"], a["k"], a["v"], None, None, a["out"], None, a["ws"], 1 << 20,
+                              a["B"], a["H"], 9, a["T"], a["d"], a["dtype"]) == INV
 
 
 def test_status_strings():

@@ -21,6 +21,17 @@ stress     5     2, 8, 8192, 128             bf16   q *= 8/sqrt(d) (logit std ~ 
                                                     k_0 = k_1, v_0 = v_1 (after the cast)
 =========  ====  ==========================  =====  ==========================================
 
+Decode workloads (few new queries against a key/value cache of T positions; the
+queries are the last Tq positions T-Tq+1..T; q [B, H, Tq, d], then k and v
+[B, H, T, d], drawn in that order with the same generator rule):
+
+===========  ====  =============================  =====  ===========================
+name         seed  B, H, Tq, T, d                 dtype  transforms / k_0, v_0
+===========  ====  =============================  =====  ===========================
+decode       6     16, 8, 1, 8192, 128            bf16   q *= 1/sqrt(d); zeros
+decode_spec  7     16, 8, 8, 8192, 128            bf16   q *= 1/sqrt(d); zeros
+===========  ====  =============================  =====  ===========================
+
 The pages fix no shapes; their experiments are language-model training runs
 with rotary embeddings, which ``lm`` stands in for.  "All zeros" and "copy
 the first key/value" are two of the k_0/v_0 choices listed under Analysis of
@@ -78,6 +89,67 @@ WORKLOADS = {
     "long": _w("long", 4, 1, 32, 16384, 128, "bf16"),
     "stress": _w("stress", 5, 2, 8, 8192, 128, "bf16", q_mult=8.0, sink="copy"),
 }
+
+
+@dataclass(frozen=True)
+class DecodeWorkload:
+    name: str
+    seed: int
+    B: int
+    H: int
+    Tq: int             # new queries, at positions T-Tq+1..T
+    T: int              # cached positions (keys/values 1..T)
+    d: int
+    dtype: str
+    q_scale: float
+    sink: str
+
+    @property
+    def torch_dtype(self):
+        return torch.float32 if self.dtype == "f32" else torch.bfloat16
+
+    @property
+    def cache_bytes(self) -> int:
+        """Bytes of k and v read once per call (the algorithmic HBM traffic that dominates)."""
+        return 2 * self.B * self.H * self.T * self.d * (4 if self.dtype == "f32" else 2)
+
+
+DECODE_WORKLOADS = {
+    "decode": DecodeWorkload("decode", 6, 16, 8, 1, 8192, 128, "bf16", 1 / math.sqrt(128), "zero"),
+    "decode_spec": DecodeWorkload("decode_spec", 7, 16, 8, 8, 8192, 128, "bf16", 1 / math.sqrt(128), "zero"),
+}
+
+
+def make_decode_inputs(w: DecodeWorkload | str, *, B=None, H=None, Tq=None, T=None, d=None, dtype=None,
+                       seed=None, sink=None):
+    """Draw (q, k, v, k0, v0) for a decode call: q [B, H, Tq, d], k and v [B, H, T, d].
+
+    Keyword overrides give smaller variants; sink is "zero" (k0 = v0 = None), "copy"
+    (k_0 = k_1, v_0 = v_1) or "random" (k0, v0 drawn after v).
+    """
+    if isinstance(w, str):
+        w = DECODE_WORKLOADS[w]
+    B = w.B if B is None else B
+    H = w.H if H is None else H
+    Tq = w.Tq if Tq is None else Tq
+    T = w.T if T is None else T
+    d = w.d if d is None else d
+    dt = w.torch_dtype if dtype is None else {"f32": torch.float32, "bf16": torch.bfloat16}[dtype]
+    seed = w.seed if seed is None else seed
+    sink = w.sink if sink is None else sink
+    g = torch.Generator("cpu").manual_seed(seed)
+    q = torch.randn((B, H, Tq, d), generator=g, dtype=torch.float32) / math.sqrt(d)
+    k = torch.randn((B, H, T, d), generator=g, dtype=torch.float32)
+    v = torch.randn((B, H, T, d), generator=g, dtype=torch.float32)
+    q, k, v = q.to(dt), k.to(dt), v.to(dt)
+    if sink == "copy":
+        k0, v0 = k[:, :, 0, :].clone(), v[:, :, 0, :].clone()
+    elif sink == "random":
+        k0 = torch.randn((B, H, d), generator=g, dtype=torch.float32).to(dt)
+        v0 = torch.randn((B, H, d), generator=g, dtype=torch.float32).to(dt)
+    else:
+        k0 = v0 = None
+    return q, k, v, k0, v0
 
 
 def rope_interleaved(x: torch.Tensor, base: float = 10000.0) -> torch.Tensor:

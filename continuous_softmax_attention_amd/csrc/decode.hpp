@@ -11,7 +11,8 @@
 // written for streaming, not for MFMA.
 //
 //   Pass 1 (decode_partial_kernel): one wave per (batch*head, split) where a split is
-//   512 consecutive positions.  Blocks of 64 positions, one position per lane:
+//   256 consecutive positions (the kernel is instantiated for at most 1, 2, 4 or 8
+//   queries, so that small Tq keep few registers and many waves in flight).  Blocks of 64 positions, one position per lane:
 //     * logits q_j . k_p for the Tq queries (lane = position; q broadcast from LDS;
 //       v_dot2_f32_bf16 for bf16);
 //     * neighbours through ds_bpermute inside the block; across blocks from the
@@ -37,7 +38,7 @@
 
 namespace csa {
 
-constexpr int kDecChunk = 512;  // positions per split
+constexpr int kDecChunk = 256;  // positions per split
 constexpr int kDecMaxQ = 8;     // queries per call
 constexpr int kDecWaves = 4;    // splits per work-group (one per wave)
 
@@ -98,7 +99,7 @@ __device__ __forceinline__ void load_lane_values(const TT* row, int lane, float 
   }
 }
 
-template <typename TT, int D>
+template <typename TT, int D, int QMAX>
 __global__ void __launch_bounds__(64 * kDecWaves) decode_partial_kernel(DecParams p) {
   static_assert(D == 16 || D == 64 || D == 128, "head dimension");
   constexpr bool F32 = sizeof(TT) == 4;
@@ -108,7 +109,8 @@ __global__ void __launch_bounds__(64 * kDecWaves) decode_partial_kernel(DecParam
   typedef float f32x4v __attribute__((ext_vector_type(4)));
   typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
 
-  __shared__ __attribute__((aligned(16))) TT qs[kDecWaves][kDecMaxQ][D];
+  __shared__ __attribute__((aligned(16))) TT qs[kDecWaves][QMAX][D];
+  static_assert(QMAX >= 1 && QMAX <= kDecMaxQ, "query bound");
 
   const int lane = threadIdx.x & 63;
   const int wv = threadIdx.x >> 6;
@@ -137,16 +139,16 @@ __global__ void __launch_bounds__(64 * kDecWaves) decode_partial_kernel(DecParam
   auto vrow = [&](int pos) -> const TT* { return pos == 0 ? V0 : Vh + (size_t)(pos - 1) * D; };
 
   // logits of position pos (per lane) for every query; 0 where the row does not exist
-  auto logits = [&](int pos, float (&a)[kDecMaxQ]) {
+  auto logits = [&](int pos, float (&a)[QMAX]) {
 #pragma unroll
-    for (int j = 0; j < kDecMaxQ; ++j) a[j] = 0.0f;
+    for (int j = 0; j < QMAX; ++j) a[j] = 0.0f;
     const TT* row = pos <= Tn ? krow(pos) : nullptr;
     if (row == nullptr) return;
     f32x4v kc[NCH];
 #pragma unroll
     for (int c = 0; c < NCH; ++c) kc[c] = *(const f32x4v*)(row + c * EPC);  // 16 bytes
 #pragma unroll
-    for (int j = 0; j < kDecMaxQ; ++j) {
+    for (int j = 0; j < QMAX; ++j) {
       if (j < Tq) {
         float acc = 0.0f;
 #pragma unroll
@@ -171,16 +173,16 @@ __global__ void __launch_bounds__(64 * kDecWaves) decode_partial_kernel(DecParam
     }
   };
   // logits of one (wave-uniform) position, lane-parallel over d; 0 if it does not exist
-  auto halo = [&](int pos, float (&a)[kDecMaxQ]) {
+  auto halo = [&](int pos, float (&a)[QMAX]) {
 #pragma unroll
-    for (int j = 0; j < kDecMaxQ; ++j) a[j] = 0.0f;
+    for (int j = 0; j < QMAX; ++j) a[j] = 0.0f;
     if (pos < 0 || pos > Tn) return;
     const TT* row = krow(pos);
     if (row == nullptr) return;
     float kv[DPL];
     load_lane_values<TT, D>(row, lane, kv);  // this lane's d elements (0 past d)
 #pragma unroll
-    for (int j = 0; j < kDecMaxQ; ++j) {
+    for (int j = 0; j < QMAX; ++j) {
       if (j < Tq) {
         float part = 0.0f;
 #pragma unroll
@@ -193,35 +195,35 @@ __global__ void __launch_bounds__(64 * kDecWaves) decode_partial_kernel(DecParam
     }
   };
 
-  float m_run[kDecMaxQ], l_run[kDecMaxQ], O[kDecMaxQ][DPL];
+  float m_run[QMAX], l_run[QMAX], O[QMAX][DPL];
 #pragma unroll
-  for (int j = 0; j < kDecMaxQ; ++j) {
+  for (int j = 0; j < QMAX; ++j) {
     m_run[j] = -__builtin_inff();
     l_run[j] = 0.0f;
 #pragma unroll
     for (int e = 0; e < DPL; ++e) O[j][e] = 0.0f;
   }
 
-  float acur[kDecMaxQ], anxt[kDecMaxQ], aleft0[kDecMaxQ];
+  float acur[QMAX], anxt[QMAX], aleft0[QMAX];
   logits(p0 + lane, acur);
   halo(p0 - 1, aleft0);  // left neighbour of the split's first position (none at p0 = 0)
 
   for (int b = 0; b < nb; ++b) {
     const int base = p0 + 64 * b;
     const int pos = base + lane;
-    float aright63[kDecMaxQ];  // right neighbour of lane 63
+    float aright63[QMAX];  // right neighbour of lane 63
     if (b + 1 < nb) {
       logits(pos + 64, anxt);
 #pragma unroll
-      for (int j = 0; j < kDecMaxQ; ++j)
+      for (int j = 0; j < QMAX; ++j)
         aright63[j] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(anxt[j]), 0));
     } else {
       halo(pend, aright63);  // position pend belongs to the next split (none past T)
     }
 
-    float wq[kDecMaxQ];
+    float wq[QMAX];
 #pragma unroll
-    for (int j = 0; j < kDecMaxQ; ++j) {
+    for (int j = 0; j < QMAX; ++j) {
       wq[j] = 0.0f;
       if (j >= Tq) continue;  // wave-uniform
       const int tj = Tn - Tq + 1 + j;                 // position of query j
@@ -278,7 +280,7 @@ __global__ void __launch_bounds__(64 * kDecWaves) decode_partial_kernel(DecParam
 #pragma unroll
       for (int kk = 0; kk < 16; ++kk) {
 #pragma unroll
-        for (int j = 0; j < kDecMaxQ; ++j) {
+        for (int j = 0; j < QMAX; ++j) {
           if (j < Tq) {
             const float s = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wq[j]), kb + kk));
 #pragma unroll
@@ -290,7 +292,7 @@ __global__ void __launch_bounds__(64 * kDecWaves) decode_partial_kernel(DecParam
 
     // the next block's left neighbour of lane 0 is this block's lane 63
 #pragma unroll
-    for (int j = 0; j < kDecMaxQ; ++j) {
+    for (int j = 0; j < QMAX; ++j) {
       aleft0[j] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(acur[j]), 63));
       acur[j] = anxt[j];
     }
@@ -298,7 +300,7 @@ __global__ void __launch_bounds__(64 * kDecWaves) decode_partial_kernel(DecParam
 
   // partial results of this split
 #pragma unroll
-  for (int j = 0; j < kDecMaxQ; ++j) {
+  for (int j = 0; j < QMAX; ++j) {
     if (j < Tq) {
       const float lsum = wave_sum(l_run[j]);
       float* dst = p.ws + (((size_t)bh * p.nsplit + sp) * Tq + j) * (D + 2);
@@ -354,8 +356,11 @@ __global__ void __launch_bounds__(64) decode_merge_kernel(DecParams p) {
 template <typename TT, int D>
 inline hipError_t launch_decode(const DecParams& prm, hipStream_t stream) {
   const int items = prm.BH * prm.nsplit;
-  hipLaunchKernelGGL((decode_partial_kernel<TT, D>), dim3((items + kDecWaves - 1) / kDecWaves),
-                     dim3(64 * kDecWaves), 0, stream, prm);
+  const dim3 grid((items + kDecWaves - 1) / kDecWaves), block(64 * kDecWaves);
+  if (prm.Tq <= 1) hipLaunchKernelGGL((decode_partial_kernel<TT, D, 1>), grid, block, 0, stream, prm);
+  else if (prm.Tq <= 2) hipLaunchKernelGGL((decode_partial_kernel<TT, D, 2>), grid, block, 0, stream, prm);
+  else if (prm.Tq <= 4) hipLaunchKernelGGL((decode_partial_kernel<TT, D, 4>), grid, block, 0, stream, prm);
+  else hipLaunchKernelGGL((decode_partial_kernel<TT, D, 8>), grid, block, 0, stream, prm);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((decode_merge_kernel<TT, D>), dim3(prm.BH * prm.Tq), dim3(64), 0, stream, prm);

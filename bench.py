@@ -185,7 +185,8 @@ def decode_legs(steps, warmup):
 
 def counters_mode(w, q, k, v, k0, v0):
     """One launch of each kernel plus a 256 MiB device-to-device copy whose HBM bytes
-    are known (256 MiB read + 256 MiB written), to scale FETCH_SIZE/WRITE_SIZE."""
+    are known (256 MiB read + 256 MiB written), to scale FETCH_SIZE/WRITE_SIZE; then one
+    csa_decode call on the decode workload."""
     import torch
 
     import continuous_softmax_attention_amd as csa
@@ -206,6 +207,13 @@ def counters_mode(w, q, k, v, k0, v0):
     if w.dtype == "bf16":
         csa.csa_forward_first_order(qd, kd, vd, k0d, v0d)
         torch.cuda.synchronize()
+    del qd, kd, vd
+    from workloads import make_decode_inputs
+
+    dq, dk, dv, _, _ = make_decode_inputs("decode")
+    dq, dk, dv = dq.to(dev), dk.to(dev), dv.to(dev)
+    csa.csa_decode(dq, dk, dv)
+    torch.cuda.synchronize()
     print(json.dumps({"counters_run": w.name, "copy_bytes": 2 * src.numel() * 4}), flush=True)
 
 

@@ -324,23 +324,38 @@ __global__ void __launch_bounds__(64) decode_merge_kernel(DecParams p) {
   const int item = blockIdx.x;  // (bh, j)
   const int bh = item / p.Tq;
   const int j = item % p.Tq;
-  const float* src = p.ws + ((size_t)bh * p.nsplit * p.Tq + j) * (D + 2);
+  const int ns = p.nsplit;
+  const float* src = p.ws + ((size_t)bh * ns * p.Tq + j) * (D + 2);
   const size_t stride = (size_t)p.Tq * (D + 2);  // between splits
+  // split maxima and weight sums with lanes over splits
   float M = -__builtin_inff();
-  for (int s = 0; s < p.nsplit; ++s) M = fmaxf(M, src[s * stride + D]);
-  float L = 0.0f, acc[DPL];
+  for (int s = lane; s < ns; s += 64) M = fmaxf(M, src[s * stride + D]);
+  M = wave_max(M);
+  float L = 0.0f;
+  for (int s = lane; s < ns; s += 64) {
+    const float ms = src[s * stride + D];
+    L += ms == -__builtin_inff() ? 0.0f : src[s * stride + D + 1] * exp2_fast(ms - M);
+  }
+  L = wave_sum(L);
+  // values with lanes over d; eight splits' loads in flight at a time
+  float acc[DPL];
 #pragma unroll
   for (int e = 0; e < DPL; ++e) acc[e] = 0.0f;
-  for (int s = 0; s < p.nsplit; ++s) {
-    const float* part = src + s * stride;
-    const float ms = part[D];
-    const float f = ms == -__builtin_inff() ? 0.0f : exp2_fast(ms - M);
-    L = __builtin_fmaf(part[D + 1], f, L);
+  for (int s0 = 0; s0 < ns; s0 += 8) {
+    float f[8], x[8][DPL];
 #pragma unroll
-    for (int e = 0; e < DPL; ++e) {
-      const int dd = lane * DPL + e;
-      if (dd < D) acc[e] = __builtin_fmaf(part[dd], f, acc[e]);
+    for (int u = 0; u < 8; ++u) {
+      const int s = min(s0 + u, ns - 1);
+      const float* part = src + s * stride;
+      const float ms = part[D];
+      f[u] = (s0 + u < ns && ms != -__builtin_inff()) ? exp2_fast(ms - M) : 0.0f;
+#pragma unroll
+      for (int e = 0; e < DPL; ++e) x[u][e] = part[min(lane * DPL + e, D - 1)];
     }
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+#pragma unroll
+      for (int e = 0; e < DPL; ++e) acc[e] = __builtin_fmaf(x[u][e], f[u], acc[e]);
   }
   const float inv = 1.0f / L;
   TT* o = (TT*)p.out + ((size_t)bh * p.Tq + j) * D;

@@ -13,7 +13,8 @@ datasets.osmarks.net).
 Every function here is pinned by ``tests/test_oracle_pins.py`` against
 something other than itself (quadrature of the defining integral, an
 independent high-precision evaluation of the simplified form, closed forms,
-invariants and limits).  No function is "parity unpinned".
+invariants and limits; the gradient against finite differences of the
+defining integral).  No function is "parity unpinned".
 """
 
 from .csa import (  # noqa: F401
@@ -25,3 +26,4 @@ from .csa import (  # noqa: F401
     std_reference,
 )
 from .first_order import csa1_reference, csa1_row  # noqa: F401
+from .backward import csa_backward_reference, csa_backward_row, dphi1, dphi2  # noqa: F401

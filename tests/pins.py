@@ -260,3 +260,77 @@ def dev1_vs_exact(ref, eps, seed=3, t=6):
     b1, _ = implied_b(ref, q_t, k_hat, t)
     b, _ = implied_b(csa_reference, q_t, k_hat, t)
     return float(np.abs(b1 - b).max())
+
+
+# ---------------------------------------------------------------- backward (gradient)
+
+def _loss_by_quadrature(q, k, v, k0, v0, do, dlse):
+    """sum_t dO_t . o_t + dlse_t lse_t with (o_t, lse_t) from the defining integral, eq. (2)."""
+    qq, kh, vh = hat(q, k, v, k0, v0)
+    total = 0.0
+    for r in range(q.shape[2]):
+        o, lse = quadrature_row(qq[r], kh, vh, r + 1)
+        total += float(do[0, 0, r] @ o) + float(dlse[0, 0, r]) * lse
+    return total
+
+
+def grad_case(seed, T=5, d=3, dv=3, scale=1.0):
+    q, k, v, k0, v0 = random_case(seed, T=T, d=d, dv=dv, scale=scale)
+    rng = np.random.default_rng(seed + 1000)
+    do = rng.standard_normal((1, 1, T, dv))
+    dlse = rng.standard_normal((1, 1, T))
+    return q, k, v, k0, v0, do, dlse
+
+
+def dev_grad_fd(ref_bwd, seed=11, scale=1.0, h=1e-5, T=5, d=3, dv=3):
+    """max |gradient - central difference of the quadrature loss| / max |gradient|.
+
+    Every entry of q, k, v, k_0, v_0 is perturbed by +-h and the loss re-evaluated
+    from the defining integral (Gauss-Legendre), never through eq. (8).  The
+    truncation error is O(h^2) and the rounding error O(1e-16/h), ~1e-10 relative.
+    """
+    q, k, v, k0, v0, do, dlse = grad_case(seed, T=T, d=d, dv=dv, scale=scale)
+    got = ref_bwd(q, k, v, do, k0, v0, dlse)
+    inputs = [q, k, v, k0, v0]
+    worst, scale_g = 0.0, max(float(np.abs(g).max()) for g in got)
+    for x, g in zip(inputs, got):
+        for idx in np.ndindex(x.shape):
+            old = x[idx]
+            x[idx] = old + h
+            lp = _loss_by_quadrature(*inputs, do, dlse)
+            x[idx] = old - h
+            lm = _loss_by_quadrature(*inputs, do, dlse)
+            x[idx] = old
+            worst = max(worst, abs((lp - lm) / (2 * h) - float(g[idx])))
+    return worst / scale_g
+
+
+def dev_grad_shift(ref_bwd, seed=12, T=24, d=5, dv=4, scale=1.5):
+    """Two symmetries of eq. (2) seen in the gradient.
+
+    v_s -> v_s + c for every position moves every o_t by c, so sum over positions
+    0..T of dv equals sum_t dO_t; k_s -> k_s + w moves every logit of query t by
+    q_t . w, which leaves o_t unchanged and moves lse_t by q_t . w, so the sum of dk
+    over positions equals sum_t dlse_t q_t.
+    """
+    q, k, v, k0, v0, do, dlse = grad_case(seed, T=T, d=d, dv=dv, scale=scale)
+    dq, dk, dv_, dk0, dv0 = ref_bwd(q, k, v, do, k0, v0, dlse)
+    sum_v = dv_[0, 0].sum(axis=0) + dv0[0, 0] - do[0, 0].sum(axis=0)
+    sum_k = dk[0, 0].sum(axis=0) + dk0[0, 0] - dlse[0, 0] @ q[0, 0]
+    return max(float(np.abs(sum_v).max()), float(np.abs(sum_k).max()))
+
+
+def dev_grad_trapezoid(ref_bwd, seed=13, T=7):
+    """q = 0 (equal logits): o_t is the trapezoid average, so dv has the closed form
+    dv_j = sum_t w_{t,j} dO_t / t with w_{t,0} = w_{t,t} = 1/2 and 1 in between."""
+    _, k, v, k0, v0, do, dlse = grad_case(seed, T=T)
+    q = np.zeros((1, 1, T, k.shape[-1]))
+    _, _, dv_, _, dv0 = ref_bwd(q, k, v, do, k0, v0, dlse)
+    expect = np.zeros((T + 1, v.shape[-1]))
+    for r in range(T):
+        t = r + 1
+        w = np.ones(t + 1)
+        w[0] = w[t] = 0.5
+        expect[: t + 1] += np.outer(w / t, do[0, 0, r])
+    got = np.concatenate([dv0[0, 0][None], dv_[0, 0]], axis=0)
+    return float(np.abs(got - expect).max())

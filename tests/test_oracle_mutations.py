@@ -9,6 +9,7 @@ import inspect
 
 import pytest
 
+import oracle.backward as oracle_backward
 import oracle.csa as oracle_csa
 import oracle.first_order as oracle_first_order
 import pins
@@ -40,8 +41,8 @@ CHECKS = [
 
 def _mutant(old, new, fn="csa_reference", module=oracle_csa):
     src = inspect.getsource(module)
-    if module is not oracle_csa:  # the module imports a helper relatively
-        src = src.replace("from .csa import _as_f64", "from oracle.csa import _as_f64")
+    if module is not oracle_csa:  # the module imports helpers relatively
+        src = src.replace("from .csa import ", "from oracle.csa import ")
     assert src.count(old) == 1, f"mutation anchor not unique: {old!r}"
     ns = {"__name__": "oracle_mutant"}
     exec(compile(src.replace(old, new), "<oracle mutant>", "exec"), ns)
@@ -95,6 +96,48 @@ def test_first_order_mutant_is_caught(name):
     ref = _mutant(*MUTATIONS1[name], fn="csa1_reference", module=oracle_first_order)
     caught = []
     for check, tol in CHECKS1:
+        try:
+            caught.append(not (check(ref) < tol))
+        except Exception:
+            caught.append(True)
+    assert any(caught), f"mutation '{name}' escaped every pin"
+
+
+# ---------------------------------------------------------------- backward reference
+
+MUTATIONS_BWD = {
+    "sign of the denominator term": ("h = (dlse_t - float(do_t @ o)) / den", "h = (dlse_t + float(do_t @ o)) / den"),
+    "lse gradient dropped": ("h = (dlse_t - float(do_t @ o)) / den", "h = (0.0 - float(do_t @ o)) / den"),
+    "derivatives swapped": ("d_right = E * (dphi1(delta) * A + dphi2(delta) * Bc)",
+                            "d_right = E * (dphi2(delta) * A + dphi1(delta) * Bc)"),
+    "left derivative sign": ("d_left = f_seg - d_right", "d_left = d_right - f_seg"),
+    "left derivative without f": ("d_left = f_seg - d_right", "d_left = -d_right"),
+    "value gradients swapped": ("dv[1:] += np.outer(E * (f1 - f2), g)", "dv[1:] += np.outer(E * f2, g)"),
+    "dphi_2 series coefficients": ("(n + 1) / math.factorial(n + 3)", "(n + 1) / math.factorial(n + 2) / 3"),
+    "dphi_2 closed form sign": ("+ 2.0 * safe) / (safe * safe * safe)", "- 2.0 * safe) / (safe * safe * safe)"),
+    "dphi_1 closed form": ("(safe * np.exp(safe) - np.expm1(safe))", "(safe * np.exp(safe) - np.exp(safe))"),
+    "dq from shifted keys": ("dq = dS @ K", "dq = dS @ np.roll(K, 1, axis=0)"),
+    "segment numerator B term": ("Bc = (v_im1 - v_i) @ g", "Bc = (v_i - v_im1) @ g"),
+}
+
+CHECKS_BWD = [
+    (lambda ref: pins.dev_grad_fd(ref, seed=21, T=4, d=2, dv=2), 1e-8),
+    (lambda ref: pins.dev_grad_fd(ref, seed=22, T=4, d=2, dv=2, scale=0.05), 1e-8),
+    (pins.dev_grad_shift, 1e-12),
+    (pins.dev_grad_trapezoid, 1e-14),
+]
+
+
+def test_unmutated_backward_reference_passes_every_check():
+    for check, tol in CHECKS_BWD:
+        assert check(oracle_backward.csa_backward_reference) < tol
+
+
+@pytest.mark.parametrize("name", sorted(MUTATIONS_BWD))
+def test_backward_mutant_is_caught(name):
+    ref = _mutant(*MUTATIONS_BWD[name], fn="csa_backward_reference", module=oracle_backward)
+    caught = []
+    for check, tol in CHECKS_BWD:
         try:
             caught.append(not (check(ref) < tol))
         except Exception:

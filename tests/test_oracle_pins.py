@@ -3,7 +3,9 @@
 Source: J. Su, "Continuous Softmax Attention" -- eq. (2)-(3) (definition),
 eq. (6) and the limits after it, identity eq. (7), eq. (8) (what the
 reference evaluates), eq. (10)-(11) (the simplified form), eq. (12)
-(standard attention) and eq. (13) (Taylor expansion of b).
+(standard attention) and eq. (13) (Taylor expansion of b); the gradient of the
+forward (the backward reference) against finite differences of the defining
+integral and two symmetries of eq. (2).
 """
 
 import json
@@ -15,7 +17,7 @@ import numpy as np
 import pytest
 
 import pins
-from oracle import csa1_reference, csa_reference, phi1, phi2, std_reference
+from oracle import csa1_reference, csa_backward_reference, csa_reference, dphi1, dphi2, phi1, phi2, std_reference
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 
@@ -206,3 +208,28 @@ def test_first_order_key_shift_invariance():
     o2, lse2 = csa1_reference(q, k + w, v, k0 + w, v0)
     assert np.abs(o2 - o).max() < 1e-12
     assert np.abs(lse2 - lse - (q @ w)).max() < 1e-12
+
+
+# ---------------------------------------------------------------- backward (gradient)
+
+@pytest.mark.parametrize("seed,scale", [(11, 1.0), (14, 0.05), (15, 3.0)])
+def test_backward_against_finite_differences_of_the_definition(seed, scale):
+    # scale 0.05 keeps every neighbour difference inside the series branch of phi_1', phi_2'
+    assert pins.dev_grad_fd(csa_backward_reference, seed=seed, scale=scale) < 1e-8
+
+
+def test_backward_shift_invariants():
+    assert pins.dev_grad_shift(csa_backward_reference) < 1e-12
+
+
+def test_backward_trapezoid_values():
+    assert pins.dev_grad_trapezoid(csa_backward_reference) < 1e-14
+
+
+def test_dphi_are_the_derivatives_of_phi():
+    x = np.concatenate([np.linspace(-6, 6, 49), [-0.26, -0.2499, 0.2499, 0.26, 1e-9, 0.0]])
+    h = 1e-6
+    for f, df in ((phi1, dphi1), (phi2, dphi2)):
+        fd = (f(x + h) - f(x - h)) / (2 * h)
+        assert (np.abs(df(x) - fd) / np.maximum(1.0, np.abs(fd))).max() < 1e-8
+    assert dphi1(0.0) == 0.5 and abs(float(dphi2(0.0)) - 1.0 / 6.0) < 1e-17

@@ -18,6 +18,10 @@ from ._lib import (  # noqa: F401
     CSA_F32,
     CSA_OK,
     CsaError,
+    csa_backward,
+    csa_backward_check,
+    csa_backward_raw,
+    csa_backward_workspace_bytes,
     csa_decode,
     csa_decode_check,
     csa_decode_raw,

@@ -42,6 +42,9 @@ _SIGS = {
     "csa_decode_check": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64, _i64,
                                         ctypes.c_int]),
     "csa_decode_workspace_bytes": (_i64, [_i64, _i64, _i64, _i64, _i64]),
+    "csa_backward": (ctypes.c_int, [_vp] * 14 + [_i64] * 5 + [ctypes.c_int, _vp]),
+    "csa_backward_check": (ctypes.c_int, [_vp] * 14 + [_i64] * 5 + [ctypes.c_int]),
+    "csa_backward_workspace_bytes": (_i64, [_i64] * 4),
     "csa_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "std_fwd": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, ctypes.c_int, _vp]),
     "std_fwd_check": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, ctypes.c_int]),
@@ -112,6 +115,23 @@ def csa_decode_check(q, k, v, k0, v0, out, lse, ws, ws_bytes, B, H, Tq, T, d, dt
 def csa_decode_workspace_bytes(B, H, Tq, T, d) -> int:
     """Bytes of workspace csa_decode needs (-1 for invalid sizes)."""
     return int(load().csa_decode_workspace_bytes(B, H, Tq, T, d))
+
+
+def csa_backward_raw(q, k, v, k0, v0, o, lse, dout, dq, dk, dv, dk0, dv0, ws, ws_bytes, B, H, T, d, dtype,
+                     stream=0) -> int:
+    return load().csa_backward(q, k, v, k0 or None, v0 or None, o, lse, dout, dq, dk, dv, dk0 or None,
+                               dv0 or None, ws, ws_bytes, B, H, T, d, dtype, stream)
+
+
+def csa_backward_check(q, k, v, k0, v0, o, lse, dout, dq, dk, dv, dk0, dv0, ws, ws_bytes, B, H, T, d,
+                       dtype) -> int:
+    return load().csa_backward_check(q, k, v, k0, v0, o, lse, dout, dq, dk, dv, dk0, dv0, ws, ws_bytes,
+                                     B, H, T, d, dtype)
+
+
+def csa_backward_workspace_bytes(B, H, T, d) -> int:
+    """Bytes of workspace csa_backward needs (-1 for invalid sizes)."""
+    return int(load().csa_backward_workspace_bytes(B, H, T, d))
 
 
 def std_fwd_raw(q, k, v, out, lse, B, H, T, d, dtype, stream=0) -> int:
@@ -281,3 +301,54 @@ def csa_decode(q, k, v, k0=None, v0=None, *, out=None, lse=None, return_lse=True
     if st != CSA_OK:
         raise CsaError(st, "csa_decode")
     return out, lse
+
+
+def csa_backward(q, k, v, o, lse, dout, k0=None, v0=None, *, sink_grads=True, dq=None, dk=None, dv=None,
+                 workspace=None, stream=None):
+    """Gradients of the causal CSA forward through libcsa (bfloat16, d in {64, 128}).
+
+    q, k, v, o (the forward's output), dout: [B, H, T, d] bfloat16 device tensors; lse: the
+    forward's [B, H, T] float32 lse; k0, v0: [B, H, d] or None (zeros).  Returns
+    (dq, dk, dv, dk0, dv0) -- dk0 and dv0 ([B, H, d]) are None when sink_grads is False.
+    ``workspace``: a device tensor of at least csa_backward_workspace_bytes(B, H, T, d) bytes
+    (allocated here when None).
+    """
+    import torch
+
+    if q.dim() != 4:
+        raise ValueError("q must be [B, H, T, d]")
+    B, H, T, d = q.shape
+    dt, dev = q.dtype, q.device
+    if dev.type != "cuda":
+        raise ValueError("csa_backward runs on the GPU only; inputs must be device tensors")
+    for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("dout", dout)):
+        _check(name, t, (B, H, T, d), dt, dev)
+    _check("lse", lse, (B, H, T), torch.float32, dev)
+    for name, t in (("k0", k0), ("v0", v0)):
+        if t is not None:
+            _check(name, t, (B, H, d), dt, dev)
+    need = csa_backward_workspace_bytes(B, H, T, d)
+    if need < 0:
+        raise CsaError(CSA_ERR_UNSUPPORTED if d not in (64, 128) else CSA_ERR_INVALID_ARG, "csa_backward (sizes)")
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    grads = []
+    for name, t in (("dq", dq), ("dk", dk), ("dv", dv)):
+        if t is None:
+            t = torch.empty_like(q)
+        else:
+            _check(name, t, (B, H, T, d), dt, dev)
+        grads.append(t)
+    dk0 = torch.empty((B, H, d), dtype=dt, device=dev) if sink_grads else None
+    dv0 = torch.empty((B, H, d), dtype=dt, device=dev) if sink_grads else None
+    st = load().csa_backward(
+        q.data_ptr(), k.data_ptr(), v.data_ptr(),
+        k0.data_ptr() if k0 is not None else None, v0.data_ptr() if v0 is not None else None,
+        o.data_ptr(), lse.data_ptr(), dout.data_ptr(),
+        grads[0].data_ptr(), grads[1].data_ptr(), grads[2].data_ptr(),
+        dk0.data_ptr() if dk0 is not None else None, dv0.data_ptr() if dv0 is not None else None,
+        workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+        B, H, T, d, _dtype_code(q), _stream_handle(stream, dev))
+    if st != CSA_OK:
+        raise CsaError(st, "csa_backward")
+    return grads[0], grads[1], grads[2], dk0, dv0

@@ -1,0 +1,674 @@
+// Backward pass of the bf16 causal CSA forward for gfx950 on 16x16x32 MFMAs.
+//
+// Method: J. Su, "Continuous Softmax Attention", eq. (10)-(11): o_t = sum_i P_{t,i} v_i with
+// P_{t,i} = e^{a_{t,i} + b_{t,i}} / Z_t, where every edge (i, i+1) (consecutive positions
+// 0..t) contributes a right term R_e = e^{a_i} phi_2(a_{i+1} - a_i) to position i and a
+// left term L_e = e^{a_{i+1}} phi_2(a_i - a_{i+1}) to position i+1.  The pages print no
+// backward; differentiating eq. (10) gives, for the loss sum_t dO_t . o_t:
+//
+//   * dR_e/da_{i+1} = dL_e/da_i = C_e = integral_0^1 s (1-s) e^{(1-s) a_i + s a_{i+1}} ds,
+//     and dR_e/da_i = R_e - C_e, dL_e/da_{i+1} = L_e - C_e;
+//   * with dP_{t,i} = dO_t . v_i, D_t = dO_t . o_t, c_e = C_e / Z_t and
+//     G_e = c_e (dP_i - dP_{i+1}), the logit gradient is a two-point stencil of edge terms
+//     on top of the softmax one:
+//         dS_{t,i} = P_{t,i} (dP_{t,i} - D_t) + G_{(i-1,i)} - G_{(i,i+1)};
+//   * dq_t = sum_i dS_{t,i} k_i,  dk_i = sum_t dS_{t,i} q_t,  dv_i = sum_t P_{t,i} dO_t,
+//     position 0 entering through k_0, v_0 (dk_0, dv_0 are the sums over t at i = 0).
+//
+// Arithmetic ("p-form", as the forward).  mu_t = log2(c^2 Z_t) = lse_t log2 e + 2 log2 c
+// (c = ln 2) comes from the forward's lse; p_i = 2^{a_i log2 e - mu_t} = e^{a_i} / (c^2 Z_t).
+// For an edge with y = (a_{i+1} - a_i) log2 e, u = 1/y and dp = p_{i+1} - p_i:
+//     R/Z = (u dp - c p_i) u,   L/Z = (c p_{i+1} - u dp) u,
+//     c_e = u^2 ((p_i + p_{i+1}) - (2/c) u dp),
+// with Taylor forms below |y| < 0.07 (R, L) and |y| < 0.25 (c_e), where the differences
+// cancel: R/Z = p_i (c^2/2 + c^3 y/6), L/Z = p_{i+1} (c^2/2 - c^3 y/6),
+// c_e = p_i (c^2/6 + c^3 y/12 + c^4 y^2/40).
+//
+// Kernels (one launch each, in this order on the caller's stream):
+//   bwd_pre   D_t = dO_t . o_t and mu_t into the workspace; zero rows standing in for a
+//             null k_0 / v_0.
+//   bwd_dq    one work-group per 128 query rows (the forward's decomposition: 8 waves x
+//             16 queries, 64-key tiles double-buffered in LDS).  Per tile S^T = K Q^T and
+//             dP^T = V dO^T on MFMAs, plus one 16-row "halo" block whose rows 0 and 1 are
+//             keys J-1 and J+64, so that every tile is self-contained; P and dS per lane
+//             (16 consecutive keys of one query, neighbours across lane groups by
+//             ds_bpermute); dQ^T += K^T dS^T with K^T through transposed LDS reads.  Also
+//             writes dS and P of position 0 per query.
+//   bwd_sink  dk_0 = sum_t dS_{t,0} q_t, dv_0 = sum_t P_{t,0} dO_t (skipped when both are null).
+//   bwd_dkdv  one work-group per 64 key rows, looping over 128-row query tiles: the same
+//             S^T, dP^T, P and dS per wave; P and dS (bf16) go through LDS so that
+//             dV^T += dO^T P and dK^T += Q^T dS contract over queries on MFMAs.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "attn16.hpp"
+
+namespace csa {
+
+struct BwdParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* k0;    // may be null (zeros)
+  const void* v0;    // may be null (zeros)
+  const void* o;     // forward output
+  const float* lse;  // forward lse (natural log)
+  const void* dout;  // dO
+  void* dq;
+  void* dk;
+  void* dv;
+  void* dk0;  // may be null (not written)
+  void* dv0;  // may be null (not written)
+  char* ws;   // workspace, bwd_workspace_bytes()
+  int B, H, T;
+};
+
+// Workspace: 512 zero bytes (two rows of up to 128 bf16), then four float arrays of
+// B*H*T: D_t, mu_t, dS_{t,0}, P_{t,0}.
+constexpr int kBwdZeroBytes = 512;
+inline int64_t bwd_workspace_bytes(int64_t BH, int64_t T) { return kBwdZeroBytes + 16 * BH * T; }
+
+struct BwdWs {
+  const char* zero;
+  float* delta;
+  float* mu;
+  float* ds0;
+  float* p0;
+};
+__device__ __forceinline__ BwdWs bwd_ws(char* ws, int BH, int T) {
+  const size_t n = (size_t)BH * (size_t)T;
+  float* f = (float*)(ws + kBwdZeroBytes);
+  return {ws, f, f + n, f + 2 * n, f + 3 * n};
+}
+
+constexpr float kMuShift = -1.0575327458897954f;  // 2 log2(ln 2)
+
+// ---------------------------------------------------------------- LDS tile layouts
+// The two 64-row layouts of attn16.hpp, as free functions of the row width.  A tile of
+// 64 rows x D columns is D/32 regions of 4 KiB (32 columns each).
+//   row layout ("K"): row r in 64-byte slot 4 (r & 3) + (r >> 4) + 16 ((r >> 2) & 3),
+//     chunk cc at position cc ^ (r & 3); read as the A operand of S^T = K Q^T.
+//   transposed layout ("V"): row r at slot r, chunk cc at position cc ^ 2 bit4(r); read
+//     with ds_read_b64_tr_b16 as 16 columns x 32 rows.
+constexpr int kRegion = 4096;
+
+// HBM byte offset, relative to the tile's first row, of LDS slot sigma (16 bytes at 16 sigma)
+template <int ROWB>
+__device__ __forceinline__ int row_layout_src(int sigma) {
+  const int region = sigma >> 8, within = sigma & 255;
+  const int gi = within >> 2;
+  const int row = 16 * (gi & 3) + 4 * (gi >> 4) + ((gi >> 2) & 3);
+  const int cc = (within & 3) ^ (row & 3);
+  return row * ROWB + (region * 4 + cc) * 16;
+}
+template <int ROWB>
+__device__ __forceinline__ int tr_layout_src(int sigma) {
+  const int region = sigma >> 8, within = sigma & 255;
+  const int row = within >> 2;
+  const int cc = (within & 3) ^ (2 * ((row >> 4) & 1));
+  return row * ROWB + (region * 4 + cc) * 16;
+}
+// LDS byte offset of chunk cc (of 16-byte chunks along the row) of row r, transposed layout
+__device__ __forceinline__ int tr_layout_at(int r, int cc) {
+  return (cc >> 2) * kRegion + r * 64 + 16 * ((cc & 3) ^ (2 * ((r >> 4) & 1)));
+}
+
+// A operand of S^T for 16-key block b, contraction step s (row layout)
+__device__ __forceinline__ bf16x8 row_read(CSA_LDS const char* tile, int kbase, int s, int b) {
+  return *(CSA_LDS const bf16x8*)(tile + kbase + s * kRegion + b * 1024);
+}
+// 16 columns (block mb) x 32 rows (16g + 8c + e, e = 0..7 for lane group g) of a transposed tile
+__device__ __forceinline__ bf16x8 tr_read(CSA_LDS const char* tile, const int (&vbase)[2], int c, int mb) {
+  CSA_LDS const char* a = tile + vbase[mb & 1] + (mb >> 1) * kRegion + 8 * c * 64;
+  const s16x4 r1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((CSA_LDS s16x4*)a);
+  const s16x4 r2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((CSA_LDS s16x4*)(a + 4 * 64));
+  const bf16x4 b1 = __builtin_bit_cast(bf16x4, r1);
+  const bf16x4 b2 = __builtin_bit_cast(bf16x4, r2);
+  return bf16x8{b1[0], b1[1], b1[2], b1[3], b2[0], b2[1], b2[2], b2[3]};
+}
+
+// One 16-byte HBM -> LDS copy per lane from a per-lane 64-bit address (lane i writes
+// lds_addr + 16 i); completion is awaited like lds_copy16's.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void lds_copy16_ptr(const char* src, unsigned lds_addr) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+               :
+               : "v"(src), "s"(lds_addr)
+               : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+// ---------------------------------------------------------------- per-element arithmetic
+// Edge (i, i+1) of one query from alpha_i, p_i, alpha_{i+1}, p_{i+1}: R/Z, L/Z and c_e as in
+// the header; all three zero when the edge does not exist (selects, so that values of
+// positions that do not exist for this query never reach the result).
+__device__ __forceinline__ void edge_grad(float al, float pl, float ar, float pr, bool exists, float& R,
+                                          float& L, float& C) {
+  constexpr float k0 = 0.2402265069591007f;     // c^2/2
+  constexpr float k1 = 0.055504108664821576f;   // c^3/6
+  constexpr float m0 = 0.08007550231970023f;    // c^2/6
+  constexpr float m1 = 0.027752054332410788f;   // c^3/12
+  constexpr float m2 = 0.005770877464577086f;   // c^4/40
+  constexpr float two_over_c = 2.8853900817779268f;
+  const float y = ar - al;
+  const float u = __builtin_amdgcn_rcpf(y);
+  const float du = (pr - pl) * u;
+  float r = __builtin_fmaf(-kLn2, pl, du) * u;
+  float l = __builtin_fmaf(kLn2, pr, -du) * u;
+  float c = __builtin_fmaf(-two_over_c, du, pl + pr) * (u * u);
+  const float ay = __builtin_fabsf(y);
+  const float rt = pl * __builtin_fmaf(y, k1, k0);
+  const float lt = pr * __builtin_fmaf(y, -k1, k0);
+  const float ct = pl * __builtin_fmaf(y, __builtin_fmaf(y, m2, m1), m0);
+  r = ay < 0.07f ? rt : r;
+  l = ay < 0.07f ? lt : l;
+  c = ay < 0.25f ? ct : c;
+  R = exists ? r : 0.0f;
+  L = exists ? l : 0.0f;
+  C = exists ? c : 0.0f;
+}
+
+// P and dS of one lane's 16 consecutive keys base+t of its query.  s/dp: logits and dO.v
+// of those keys; sl, dpl and sr, dpr: the same for keys base-1 and base+16.  Key base+t is
+// visible iff t <= lim.  Also returns P and dS of key base-1 as they follow from its right
+// edge alone: exact when key base-1 is position 0 (which has no left edge).
+__device__ __forceinline__ void tile_grad(const float (&s)[16], const float (&dp)[16], float sl, float dpl,
+                                          float sr, float dpr, float mu, float delta, int lim, float (&P)[16],
+                                          float (&dS)[16], float& p_left, float& ds_left) {
+  auto alpha = [&](float x) { return __builtin_fmaf(x, kLog2e, -mu); };
+  float aC = alpha(sl), pC = exp2_fast(aC), dC = dpl;
+  float aN = alpha(s[0]), pN = exp2_fast(aN), dN = dp[0];
+  float R, L, C;
+  edge_grad(aC, pC, aN, pN, 0 <= lim, R, L, C);
+  float G = C * (dC - dN);
+  p_left = R;
+  ds_left = __builtin_fmaf(R, dC - delta, -G);
+  float Lprev = L, Gprev = G;
+  aC = aN;
+  pC = pN;
+  dC = dN;
+#pragma unroll
+  for (int t = 0; t < 16; ++t) {
+    if (t < 15) {
+      aN = alpha(s[t + 1]);
+      dN = dp[t + 1];
+    } else {
+      aN = alpha(sr);
+      dN = dpr;
+    }
+    pN = exp2_fast(aN);
+    edge_grad(aC, pC, aN, pN, t + 1 <= lim, R, L, C);
+    G = C * (dC - dN);
+    const float pt = Lprev + R;
+    P[t] = pt;
+    dS[t] = __builtin_fmaf(pt, dC - delta, Gprev - G);
+    Lprev = L;
+    Gprev = G;
+    aC = aN;
+    pC = pN;
+    dC = dN;
+  }
+}
+
+// ---------------------------------------------------------------- shared per-wave pieces
+template <int D>
+struct WaveTile {
+  static constexpr int CH = D / 8;
+  static constexpr int ROWB = 2 * D;
+  static constexpr int NSTEP = D / 32;
+  static constexpr int NMB = D / 16;
+  static constexpr int TILE = kTile * ROWB;  // 64 rows
+  static constexpr int HALO = 16 * ROWB;     // 16 rows: keys J-1, J+64, then 14 zero rows
+};
+
+// LDS read bases of a lane (the attn16 forms)
+__device__ __forceinline__ int row_kbase(int n, int g) { return (4 * (n & 3) + (n >> 2)) * 64 + 16 * (g ^ (n & 3)); }
+__device__ __forceinline__ void tr_vbase(int n, int g, int (&vb)[2]) {
+#pragma unroll
+  for (int par = 0; par < 2; ++par) {
+    const int cc = 2 * par + ((n >> 1) & 1);
+    vb[par] = (16 * g + (n >> 2)) * 64 + 16 * (cc ^ (2 * (g & 1))) + 8 * (n & 1);
+  }
+}
+
+// S^T (or dP^T) of 16 queries x 64 keys from a row-layout tile, plus the halo block
+// (rows 0, 1 = keys J-1, J+64) -> lanes g = 0 get them in elements 0 and 1.
+template <int D>
+__device__ __forceinline__ void logits_tile(CSA_LDS const char* tile, CSA_LDS const char* halo, int kbase,
+                                            int hoff, const bf16x8 (&b)[D / 32], float (&s)[16], f32x4& H) {
+  constexpr int NSTEP = D / 32;
+  f32x4 S[4];
+#pragma unroll
+  for (int blk = 0; blk < 4; ++blk) {
+    S[blk] = f32x4{};
+#pragma unroll
+    for (int st = 0; st < NSTEP; ++st)
+      S[blk] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(row_read(tile, kbase, st, blk), b[st], S[blk], 0, 0, 0);
+  }
+  H = f32x4{};
+#pragma unroll
+  for (int st = 0; st < NSTEP; ++st) {
+    const bf16x8 a = *(CSA_LDS const bf16x8*)(halo + hoff + st * 64);
+    H = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b[st], H, 0, 0, 0);
+  }
+#pragma unroll
+  for (int t = 0; t < 16; ++t) s[t] = S[t >> 2][t & 3];
+}
+
+// Neighbour values of a lane's 16 keys: key base-1 from the previous lane group (or, for
+// g = 0, the halo's key J-1), key base+16 from the next (or, for g = 3, key J+64).
+__device__ __forceinline__ void neighbours(const float (&x)[16], const f32x4& H, int n, int g, float& left,
+                                           float& right) {
+  const int lane = (g << 4) | n;
+  const int lane_up = (lane - 16) & 63, lane_dn = (lane + 16) & 63;
+  const float l = __int_as_float(__builtin_amdgcn_ds_bpermute(lane_up << 2, __float_as_int(x[15])));
+  const float r = __int_as_float(__builtin_amdgcn_ds_bpermute(lane_dn << 2, __float_as_int(x[0])));
+  const float h1 = __int_as_float(__builtin_amdgcn_ds_bpermute(n << 2, __float_as_int(H[1])));
+  left = g == 0 ? H[0] : l;
+  right = g == 3 ? h1 : r;
+}
+
+// Stage the halo rows: K rows (J-1, J+64) into halo rows 0, 1 and the same V rows into the
+// V halo, from per-lane addresses (row J-1 of position 0 is k0 / v0).  Wave-uniform caller.
+template <int D>
+__device__ __forceinline__ void stage_halo(CSA_LDS char* khalo, CSA_LDS char* vhalo, const char* kleft,
+                                           const char* kright, const char* vleft, const char* vright, int lane) {
+  constexpr int CH = D / 8;
+  if (lane < 2 * CH) {
+    const int c = lane % CH;
+    const bool right = lane >= CH;
+    lds_copy16_ptr((right ? kright : kleft) + 16 * c,
+                   __builtin_amdgcn_readfirstlane((unsigned)(uintptr_t)khalo));
+    lds_copy16_ptr((right ? vright : vleft) + 16 * c,
+                   __builtin_amdgcn_readfirstlane((unsigned)(uintptr_t)vhalo));
+  }
+}
+
+// Stage 64 rows starting at row0 (rows past T repeat row T-1, so every address stays inside
+// the tensor) into dst; off = the calling thread's source offset for round 0 of the layout.
+template <int D>
+__device__ __forceinline__ void stage_tile(CSA_LDS char* dst, const char* src, int row0, int off, int Tn,
+                                           int wave) {
+  constexpr int ROWB = 2 * D, CH = D / 8, ROUNDS = (kTile * CH + 511) / 512;
+  const int base_row = min(row0, Tn - 1);
+  const int row = off / ROWB;
+  off += (min(row0 + row, Tn - 1) - base_row - row) * ROWB;
+  const char* base = src + (size_t)base_row * ROWB;
+#pragma unroll
+  for (int r = 0; r < ROUNDS; ++r) {
+    if (r * 512 + wave * 64 < kTile * CH) {  // wave-uniform
+      const unsigned d = __builtin_amdgcn_readfirstlane((unsigned)(uintptr_t)(dst + (r * 512 + wave * 64) * 16));
+      lds_copy16(base + 128 * r, off, d);
+    }
+  }
+}
+
+// ---------------------------------------------------------------- kernels
+template <int D>
+__global__ void __launch_bounds__(256) bwd_pre_kernel(BwdParams p) {
+  constexpr int CH = D / 8;
+  constexpr int RPW = 64 / CH;  // rows per wave
+  const int BH = p.B * p.H, T = p.T;
+  const BwdWs w = bwd_ws(p.ws, BH, T);
+  if (blockIdx.x == 0 && threadIdx.x < kBwdZeroBytes / 4) ((float*)p.ws)[threadIdx.x] = 0.0f;
+  const int lane = threadIdx.x & 63;
+  const int64_t nrows = (int64_t)BH * T;
+  const int64_t row = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * RPW + lane / CH;
+  const int c = lane % CH;
+  float acc = 0.0f;
+  if (row < nrows) {
+    const bf16x8 a = *(const bf16x8*)((const bf16*)p.dout + row * D + c * 8);
+    const bf16x8 b = *(const bf16x8*)((const bf16*)p.o + row * D + c * 8);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc = __builtin_fmaf((float)a[e], (float)b[e], acc);
+  }
+#pragma unroll
+  for (int m = 1; m < CH; m <<= 1) acc += __shfl_xor(acc, m);
+  if (row < nrows && c == 0) {
+    w.delta[row] = acc;
+    w.mu[row] = __builtin_fmaf(p.lse[row], kLog2e, kMuShift);
+  }
+}
+
+template <int D>
+__global__ void __launch_bounds__(512, 2) bwd_dq_kernel(BwdParams p) {
+  using WT = WaveTile<D>;
+  constexpr int CH = WT::CH, ROWB = WT::ROWB, NSTEP = WT::NSTEP, NMB = WT::NMB;
+  constexpr int TILE = WT::TILE, HALO = WT::HALO;
+  constexpr int BUF = 3 * TILE + 2 * HALO;  // Krow | Ktr | Vrow | Khalo | Vhalo
+  static_assert(D == 64 || D == 128, "head dimension");
+
+  __shared__ __attribute__((aligned(1024))) char smem[2 * BUF];
+  CSA_LDS char* lds = (CSA_LDS char*)smem;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int n = lane & 15, g = lane >> 4;
+  const int Tn = p.T, BH = p.B * p.H;
+  const int nqb = (Tn + kBlockRows - 1) / kBlockRows;
+  const int bh = blockIdx.x % BH;
+  const int qb = nqb - 1 - blockIdx.x / BH;  // longest query blocks first
+  const int q0 = qb * kBlockRows;
+  const int qw = q0 + 16 * wave;
+  const int qr = qw + n;
+  const bool wave_rows = qw < Tn;
+  const int jw = wave_rows ? min(qw + 15, Tn - 1) / kTile : -1;
+  const int jmax = min(q0 + kBlockRows - 1, Tn - 1) / kTile;
+  const BwdWs ws = bwd_ws(p.ws, BH, Tn);
+
+  const size_t head = (size_t)bh * (size_t)Tn * D;
+  const char* Kg = (const char*)((const bf16*)p.k + head);
+  const char* Vg = (const char*)((const bf16*)p.v + head);
+  const char* K0 = p.k0 ? (const char*)((const bf16*)p.k0 + (size_t)bh * D) : ws.zero;
+  const char* V0 = p.v0 ? (const char*)((const bf16*)p.v0 + (size_t)bh * D) : ws.zero;
+
+  // zero rows 2..15 of both halo buffers (never written again)
+  for (int i = tid; i < 2 * 2 * 14 * CH; i += 512) {
+    const int buf = i / (2 * 14 * CH), rest = i % (2 * 14 * CH);
+    const int which = rest / (14 * CH), chunk = rest % (14 * CH);
+    *(CSA_LDS f32x4*)(lds + buf * BUF + 3 * TILE + which * HALO + 2 * ROWB + 16 * chunk) = f32x4{};
+  }
+
+  const int roff = row_layout_src<ROWB>(tid), toff = tr_layout_src<ROWB>(tid);
+  auto stage = [&](int buf, int tile) {
+    CSA_LDS char* b = lds + buf * BUF;
+    stage_tile<D>(b, Kg, tile * kTile, roff, Tn, wave);
+    stage_tile<D>(b + TILE, Kg, tile * kTile, toff, Tn, wave);
+    stage_tile<D>(b + 2 * TILE, Vg, tile * kTile, roff, Tn, wave);
+    if (wave == 0) {
+      const int J = tile * kTile;
+      const int rr = min(J + kTile, Tn - 1);
+      stage_halo<D>(b + 3 * TILE, b + 3 * TILE + HALO, J > 0 ? Kg + (size_t)(J - 1) * ROWB : K0,
+                    Kg + (size_t)rr * ROWB, J > 0 ? Vg + (size_t)(J - 1) * ROWB : V0, Vg + (size_t)rr * ROWB, lane);
+    }
+  };
+
+  // per-query operands: Q and dO rows (chunk 4s + g), mu_t and D_t
+  bf16x8 qreg[NSTEP], dreg[NSTEP];
+  const int rowc = min(qr, Tn - 1);
+  {
+    const bf16* Qg = (const bf16*)p.q + head + (size_t)rowc * D;
+    const bf16* Dg = (const bf16*)p.dout + head + (size_t)rowc * D;
+#pragma unroll
+    for (int s = 0; s < NSTEP; ++s) {
+      qreg[s] = *(const bf16x8*)(Qg + (4 * s + g) * 8);
+      dreg[s] = *(const bf16x8*)(Dg + (4 * s + g) * 8);
+    }
+  }
+  const float mu = ws.mu[(size_t)bh * Tn + rowc];
+  const float delta = ws.delta[(size_t)bh * Tn + rowc];
+
+  const int kbase = row_kbase(n, g);
+  int vbase[2];
+  tr_vbase(n, g, vbase);
+  const int hoff = n * ROWB + 16 * g;
+
+  f32x4 acc[NMB];
+#pragma unroll
+  for (int mb = 0; mb < NMB; ++mb) acc[mb] = f32x4{};
+  float ds0 = 0.0f, p0 = 0.0f;  // position 0 (lanes g = 0)
+
+  stage(0, 0);
+  wait_vmem();
+  __syncthreads();
+  for (int j = 0; j <= jmax; ++j) {
+    if (j + 1 <= jmax) stage((j + 1) & 1, j + 1);
+    if (j <= jw) {
+      CSA_LDS const char* b = lds + (j & 1) * BUF;
+      float s[16], dp[16];
+      f32x4 Hs, Hd;
+      logits_tile<D>(b, b + 3 * TILE, kbase, hoff, qreg, s, Hs);
+      logits_tile<D>(b + 2 * TILE, b + 3 * TILE + HALO, kbase, hoff, dreg, dp, Hd);
+      float sl, sr, dl, dr;
+      neighbours(s, Hs, n, g, sl, sr);
+      neighbours(dp, Hd, n, g, dl, dr);
+      int lim = qr < Tn ? qr - (j * kTile + 16 * g) : -2;
+      float P[16], dS[16], pl, dsl;
+      tile_grad(s, dp, sl, dl, sr, dr, mu, delta, lim, P, dS, pl, dsl);
+      if (j == 0) {
+        p0 = pl;
+        ds0 = dsl;
+      }
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        bf16x8 B;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) B[e] = (bf16)dS[8 * c + e];
+#pragma unroll
+        for (int mb = 0; mb < NMB; ++mb)
+          acc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(tr_read(b + TILE, vbase, c, mb), B, acc[mb], 0, 0, 0);
+      }
+    }
+    wait_vmem();
+    __syncthreads();
+  }
+  if (!wave_rows) return;
+
+  // dq = (K^T dS^T)^T + dS_{t,0} k_0;  position 0's P and dS for the k_0 / v_0 gradients
+  const float ds0q = __int_as_float(__builtin_amdgcn_ds_bpermute(n << 2, __float_as_int(ds0)));
+  if (qr < Tn) {
+    const bf16* k0v = p.k0 ? (const bf16*)p.k0 + (size_t)bh * D : nullptr;
+    bf16* out = (bf16*)p.dq + head + (size_t)qr * D;
+#pragma unroll
+    for (int mb = 0; mb < NMB; ++mb) {
+      const int d0 = 16 * mb + 4 * g;
+      float o4[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        o4[r] = acc[mb][r];
+        if (k0v) o4[r] = __builtin_fmaf(ds0q, (float)k0v[d0 + r], o4[r]);
+      }
+      *(bf16x4*)(out + d0) = bf16x4{(bf16)o4[0], (bf16)o4[1], (bf16)o4[2], (bf16)o4[3]};
+    }
+    if (g == 0) {
+      ws.ds0[(size_t)bh * Tn + qr] = ds0;
+      ws.p0[(size_t)bh * Tn + qr] = p0;
+    }
+  }
+}
+
+// dk_0 = sum_t dS_{t,0} q_t and dv_0 = sum_t P_{t,0} dO_t: one work-group per (b, h)
+template <int D>
+__global__ void __launch_bounds__(256) bwd_sink_kernel(BwdParams p) {
+  constexpr int CH = D / 8;
+  constexpr int NPH = 256 / CH;  // row phases
+  __shared__ float red[2][NPH][D];
+  const int BH = p.B * p.H, Tn = p.T;
+  const BwdWs ws = bwd_ws(p.ws, BH, Tn);
+  const int bh = blockIdx.x;
+  const int c = threadIdx.x % CH, ph = threadIdx.x / CH;
+  const size_t head = (size_t)bh * (size_t)Tn * D;
+  float ak[8] = {}, av[8] = {};
+  for (int t = ph; t < Tn; t += NPH) {
+    const float a = ws.ds0[(size_t)bh * Tn + t];
+    const float b = ws.p0[(size_t)bh * Tn + t];
+    const bf16x8 qv = *(const bf16x8*)((const bf16*)p.q + head + (size_t)t * D + 8 * c);
+    const bf16x8 dv = *(const bf16x8*)((const bf16*)p.dout + head + (size_t)t * D + 8 * c);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      ak[e] = __builtin_fmaf(a, (float)qv[e], ak[e]);
+      av[e] = __builtin_fmaf(b, (float)dv[e], av[e]);
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    red[0][ph][8 * c + e] = ak[e];
+    red[1][ph][8 * c + e] = av[e];
+  }
+  __syncthreads();
+  if (threadIdx.x < 2 * D) {
+    const int which = threadIdx.x / D, d = threadIdx.x % D;
+    float sum = 0.0f;
+    for (int i = 0; i < NPH; ++i) sum += red[which][i][d];
+    bf16* dst = (bf16*)(which == 0 ? p.dk0 : p.dv0);
+    if (dst) dst[(size_t)bh * D + d] = (bf16)sum;
+  }
+}
+
+template <int D>
+__global__ void __launch_bounds__(512, 2) bwd_dkdv_kernel(BwdParams p) {
+  using WT = WaveTile<D>;
+  constexpr int CH = WT::CH, ROWB = WT::ROWB, NSTEP = WT::NSTEP, NMB = WT::NMB;
+  constexpr int TILE = WT::TILE, HALO = WT::HALO;
+  constexpr int PT = 2 * 64 * 128;  // P or dS: 128 queries x 64 keys bf16 (two 64-row tiles)
+  // Krow | Vrow | Khalo | Vhalo | Q (2 tiles) | dO (2 tiles) | P | dS
+  constexpr int OFF_V = TILE, OFF_KH = 2 * TILE, OFF_VH = 2 * TILE + HALO, OFF_Q = 2 * TILE + 2 * HALO;
+  constexpr int OFF_DO = OFF_Q + 2 * TILE, OFF_P = OFF_DO + 2 * TILE, OFF_DS = OFF_P + PT;
+  constexpr int LDS_BYTES = OFF_DS + PT;
+  constexpr int KPW = NMB == 8 ? 4 : 2;  // 16-key output blocks per wave
+  static_assert(D == 64 || D == 128, "head dimension");
+
+  __shared__ __attribute__((aligned(1024))) char smem[LDS_BYTES];
+  CSA_LDS char* lds = (CSA_LDS char*)smem;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int n = lane & 15, g = lane >> 4;
+  const int Tn = p.T, BH = p.B * p.H;
+  const int bh = blockIdx.x % BH;
+  const int kb = blockIdx.x / BH;  // block 0 (the most queries) first
+  const int J = kb * kTile;
+  const BwdWs ws = bwd_ws(p.ws, BH, Tn);
+
+  const size_t head = (size_t)bh * (size_t)Tn * D;
+  const char* Kg = (const char*)((const bf16*)p.k + head);
+  const char* Vg = (const char*)((const bf16*)p.v + head);
+  const char* Qg = (const char*)((const bf16*)p.q + head);
+  const char* Og = (const char*)((const bf16*)p.dout + head);
+  const char* K0 = p.k0 ? (const char*)((const bf16*)p.k0 + (size_t)bh * D) : ws.zero;
+  const char* V0 = p.v0 ? (const char*)((const bf16*)p.v0 + (size_t)bh * D) : ws.zero;
+
+  for (int i = tid; i < 2 * 14 * CH; i += 512) {
+    const int which = i / (14 * CH), chunk = i % (14 * CH);
+    *(CSA_LDS f32x4*)(lds + OFF_KH + which * HALO + 2 * ROWB + 16 * chunk) = f32x4{};
+  }
+  const int roff = row_layout_src<ROWB>(tid), toff = tr_layout_src<ROWB>(tid);
+  // the key block and its halo rows, once
+  stage_tile<D>(lds, Kg, J, roff, Tn, wave);
+  stage_tile<D>(lds + OFF_V, Vg, J, roff, Tn, wave);
+  if (wave == 0) {
+    const int rr = min(J + kTile, Tn - 1);
+    stage_halo<D>(lds + OFF_KH, lds + OFF_VH, J > 0 ? Kg + (size_t)(J - 1) * ROWB : K0, Kg + (size_t)rr * ROWB,
+                  J > 0 ? Vg + (size_t)(J - 1) * ROWB : V0, Vg + (size_t)rr * ROWB, lane);
+  }
+
+  const int kbase = row_kbase(n, g);
+  int vbase[2];
+  tr_vbase(n, g, vbase);
+  const int hoff = n * ROWB + 16 * g;
+  // this wave's output blocks: 16 d-columns mb, 16-key blocks kc0 .. kc0 + KPW - 1
+  const int mb = NMB == 8 ? wave : (wave & 3);
+  const int kc0 = NMB == 8 ? 0 : 2 * (wave >> 2);
+  f32x4 dK[KPW], dV[KPW];
+#pragma unroll
+  for (int i = 0; i < KPW; ++i) dK[i] = dV[i] = f32x4{};
+
+  // P / dS rows of this wave in LDS: query tile row 16 wave + n = tile (wave >> 2), row 16 (wave & 3) + n
+  const int prow = 16 * (wave & 3) + n;
+  const int pt_off = (wave >> 2) * (PT / 2);
+
+  const int i0 = J / kBlockRows;
+  const int i1 = (Tn - 1) / kBlockRows;
+  for (int it = i0; it <= i1; ++it) {
+    const int Q0 = it * kBlockRows;
+    // both 64-row halves always (rows past T repeat row T-1): the dK / dV products read
+    // all 128 rows, with P = dS = 0 on rows past T
+    stage_tile<D>(lds + OFF_Q, Qg, Q0, toff, Tn, wave);
+    stage_tile<D>(lds + OFF_Q + TILE, Qg, Q0 + kTile, toff, Tn, wave);
+    stage_tile<D>(lds + OFF_DO, Og, Q0, toff, Tn, wave);
+    stage_tile<D>(lds + OFF_DO + TILE, Og, Q0 + kTile, toff, Tn, wave);
+
+    const int qr = Q0 + 16 * wave + n;
+    const int rowc = min(qr, Tn - 1);
+    bf16x8 qreg[NSTEP], dreg[NSTEP];
+#pragma unroll
+    for (int s = 0; s < NSTEP; ++s) {
+      qreg[s] = *(const bf16x8*)(Qg + (size_t)rowc * ROWB + (4 * s + g) * 16);
+      dreg[s] = *(const bf16x8*)(Og + (size_t)rowc * ROWB + (4 * s + g) * 16);
+    }
+    const float mu = ws.mu[(size_t)bh * Tn + rowc];
+    const float delta = ws.delta[(size_t)bh * Tn + rowc];
+    if (it == i0) {  // the key block and halo (first iteration only) must have landed
+      wait_vmem();
+      __syncthreads();
+    }
+    float s[16], dp[16];
+    f32x4 Hs, Hd;
+    logits_tile<D>(lds, lds + OFF_KH, kbase, hoff, qreg, s, Hs);
+    logits_tile<D>(lds + OFF_V, lds + OFF_VH, kbase, hoff, dreg, dp, Hd);
+    float sl, sr, dl, dr;
+    neighbours(s, Hs, n, g, sl, sr);
+    neighbours(dp, Hd, n, g, dl, dr);
+    const int lim = qr < Tn ? qr - (J + 16 * g) : -2;
+    float P[16], dS[16], pl, dsl;
+    tile_grad(s, dp, sl, dl, sr, dr, mu, delta, lim, P, dS, pl, dsl);
+    // keys 16g + 8h + e = chunks 2g + h of the P / dS row
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      bf16x8 pv, dv;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        pv[e] = (bf16)P[8 * h + e];
+        dv[e] = (bf16)dS[8 * h + e];
+      }
+      const int at = pt_off + tr_layout_at(prow, 2 * g + h);
+      *(CSA_LDS bf16x8*)(lds + OFF_P + at) = pv;
+      *(CSA_LDS bf16x8*)(lds + OFF_DS + at) = dv;
+    }
+    wait_vmem();
+    __syncthreads();
+    // dV^T += dO^T P and dK^T += Q^T dS over the tile's 128 queries (4 steps of 32)
+#pragma unroll
+    for (int st = 0; st < 2; ++st) {
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        const bf16x8 aq = tr_read(lds + OFF_Q + st * TILE, vbase, c, mb);
+        const bf16x8 ad = tr_read(lds + OFF_DO + st * TILE, vbase, c, mb);
+#pragma unroll
+        for (int i = 0; i < KPW; ++i) {
+          const bf16x8 bs = tr_read(lds + OFF_DS + st * (PT / 2), vbase, c, kc0 + i);
+          const bf16x8 bp = tr_read(lds + OFF_P + st * (PT / 2), vbase, c, kc0 + i);
+          dK[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aq, bs, dK[i], 0, 0, 0);
+          dV[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ad, bp, dV[i], 0, 0, 0);
+        }
+      }
+    }
+    __syncthreads();
+  }
+
+  // lane (n, g) holds dK^T[16 mb + 4g + r][key 16 kc + n]
+#pragma unroll
+  for (int i = 0; i < KPW; ++i) {
+    const int row = J + 16 * (kc0 + i) + n;
+    if (row < Tn) {
+      const int d0 = 16 * mb + 4 * g;
+      bf16* ok = (bf16*)p.dk + head + (size_t)row * D + d0;
+      bf16* ov = (bf16*)p.dv + head + (size_t)row * D + d0;
+      *(bf16x4*)ok = bf16x4{(bf16)dK[i][0], (bf16)dK[i][1], (bf16)dK[i][2], (bf16)dK[i][3]};
+      *(bf16x4*)ov = bf16x4{(bf16)dV[i][0], (bf16)dV[i][1], (bf16)dV[i][2], (bf16)dV[i][3]};
+    }
+  }
+}
+
+template <int D>
+inline hipError_t launch_backward(const BwdParams& prm, hipStream_t stream) {
+  const int64_t BH = (int64_t)prm.B * prm.H;
+  const int64_t rows = BH * prm.T;
+  const int rpb = 4 * (64 / (D / 8));  // rows per pre block
+  hipLaunchKernelGGL((bwd_pre_kernel<D>), dim3((unsigned)((rows + rpb - 1) / rpb)), dim3(256), 0, stream, prm);
+  const int nqb = (prm.T + kBlockRows - 1) / kBlockRows;
+  hipLaunchKernelGGL((bwd_dq_kernel<D>), dim3((unsigned)(nqb * BH)), dim3(512), 0, stream, prm);
+  if (prm.dk0 != nullptr || prm.dv0 != nullptr)
+    hipLaunchKernelGGL((bwd_sink_kernel<D>), dim3((unsigned)BH), dim3(256), 0, stream, prm);
+  const int nkb = (prm.T + kTile - 1) / kTile;
+  hipLaunchKernelGGL((bwd_dkdv_kernel<D>), dim3((unsigned)(nkb * BH)), dim3(512), 0, stream, prm);
+  return hipGetLastError();
+}
+
+}  // namespace csa

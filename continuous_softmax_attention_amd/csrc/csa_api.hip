@@ -1,7 +1,9 @@
-// C-ABI entry points of libcsa: csa_forward and its validation.
+// C-ABI entry points of libcsa: csa_forward, csa_forward_first_order, csa_decode and
+// csa_backward, each with its argument validation.
 #include <hip/hip_runtime.h>
 
 #include "attn16.hpp"
+#include "bwd16.hpp"
 #include "decode.hpp"
 #include "attn_fwd.hpp"
 #include "csa.h"
@@ -105,5 +107,32 @@ extern "C" int csa_decode(const void* q, const void* k, const void* v, const voi
     else if (d == 64) e = csa::launch_decode<csa::bf16, 64>(p, s);
     else e = csa::launch_decode<csa::bf16, 128>(p, s);
   }
+  return e == hipSuccess ? CSA_OK : CSA_ERR_HIP;
+}
+
+extern "C" int64_t csa_backward_workspace_bytes(int64_t B, int64_t H, int64_t T, int64_t d) {
+  return csa::backward_workspace_bytes(B, H, T, d);
+}
+
+extern "C" int csa_backward_check(const void* q, const void* k, const void* v, const void* k0, const void* v0,
+                                  const void* o, const float* lse, const void* dout, const void* dq,
+                                  const void* dk, const void* dv, const void* dk0, const void* dv0,
+                                  const void* workspace, int64_t workspace_bytes, int64_t B, int64_t H,
+                                  int64_t T, int64_t d, int dtype) {
+  return csa::validate_backward(q, k, v, k0, v0, o, lse, dout, dq, dk, dv, dk0, dv0, workspace,
+                                workspace_bytes, B, H, T, d, dtype);
+}
+
+extern "C" int csa_backward(const void* q, const void* k, const void* v, const void* k0, const void* v0,
+                            const void* o, const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                            void* dk0, void* dv0, void* workspace, int64_t workspace_bytes, int64_t B,
+                            int64_t H, int64_t T, int64_t d, int dtype, void* stream) {
+  const int st = csa::validate_backward(q, k, v, k0, v0, o, lse, dout, dq, dk, dv, dk0, dv0, workspace,
+                                        workspace_bytes, B, H, T, d, dtype);
+  if (st != CSA_OK) return st;
+  csa::BwdParams p{q, k, v, k0, v0, o, lse, dout, dq, dk, dv, dk0, dv0, (char*)workspace,
+                   (int)B, (int)H, (int)T};
+  const hipError_t e = d == 64 ? csa::launch_backward<64>(p, (hipStream_t)stream)
+                               : csa::launch_backward<128>(p, (hipStream_t)stream);
   return e == hipSuccess ? CSA_OK : CSA_ERR_HIP;
 }

@@ -97,6 +97,45 @@ inline int validate_decode(const void* q, const void* k, const void* v, const vo
   return CSA_OK;
 }
 
+// Checks of the backward entry points: bf16 only, d in {64, 128}; q, k, v, o, dO, dq, dk,
+// dv [B, H, T, d] and the workspace required; k0, v0, dk0, dv0 optional; no output may
+// overlap another output or any input.
+inline int64_t backward_workspace_bytes(int64_t B, int64_t H, int64_t T, int64_t d) {
+  if (B < 1 || H < 1 || T < 1) return -1;
+  if (d != 64 && d != 128) return -1;
+  const int64_t kMax32 = (int64_t(1) << 31) - 1;
+  if (T > kMax32 / 2 || B > kMax32 || H > kMax32 || B * H > kMax32 / T) return -1;  // B*H*T rows < 2^31
+  return 512 + 16 * B * H * T;
+}
+
+inline int validate_backward(const void* q, const void* k, const void* v, const void* k0, const void* v0,
+                             const void* o, const float* lse, const void* dout, const void* dq, const void* dk,
+                             const void* dv, const void* dk0, const void* dv0, const void* ws, int64_t ws_bytes,
+                             int64_t B, int64_t H, int64_t T, int64_t d, int dtype) {
+  if (dtype != CSA_BF16) return CSA_ERR_UNSUPPORTED;
+  if (d != 64 && d != 128) return CSA_ERR_UNSUPPORTED;
+  if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv || !ws) return CSA_ERR_INVALID_ARG;
+  const int64_t need = backward_workspace_bytes(B, H, T, d);
+  if (need < 0 || ws_bytes < need) return CSA_ERR_INVALID_ARG;
+  for (const void* p : {q, k, v, o, dout, dq, dk, dv, ws})
+    if (!aligned(p, 16)) return CSA_ERR_INVALID_ARG;
+  for (const void* p : {k0, v0, dk0, dv0})
+    if (p && !aligned(p, 16)) return CSA_ERR_INVALID_ARG;
+  if (!aligned(lse, 4)) return CSA_ERR_INVALID_ARG;
+  const int64_t big = B * H * T * d * 2, small = B * H * d * 2;
+  const Span ins[8] = {span_of(q, big),  span_of(k, big),  span_of(v, big),  span_of(k0, small),
+                       span_of(v0, small), span_of(o, big), span_of(lse, B * H * T * 4), span_of(dout, big)};
+  const Span outs[6] = {span_of(dq, big),    span_of(dk, big),    span_of(dv, big),
+                        span_of(dk0, small), span_of(dv0, small), span_of(ws, need)};
+  for (int i = 0; i < 6; ++i) {
+    for (const Span& s : ins)
+      if (overlaps(outs[i], s)) return CSA_ERR_INVALID_ARG;
+    for (int j = i + 1; j < 6; ++j)
+      if (overlaps(outs[i], outs[j])) return CSA_ERR_INVALID_ARG;
+  }
+  return CSA_OK;
+}
+
 inline const char* status_string(int s) {
   switch (s) {
     case CSA_OK: return "ok";

@@ -1,6 +1,7 @@
 /*
- * libcsa -- causal forward pass of continuous softmax attention on AMD
- * Instinct MI355X (gfx950).
+ * libcsa -- causal continuous softmax attention on AMD Instinct MI355X (gfx950):
+ * the forward pass, its first-order variant, few-query decoding against a cache, and the
+ * backward pass.
  *
  * Method: J. Su, "Continuous Softmax Attention" (Scientific Spaces; English
  * translation on tylerromero.com).  Keys and values are linearly interpolated
@@ -143,6 +144,53 @@ int csa_decode_check(const void* q, const void* k, const void* v, const void* k0
 
 /* Workspace bytes csa_decode needs for these sizes, or -1 if the sizes are invalid. */
 int64_t csa_decode_workspace_bytes(int64_t B, int64_t H, int64_t Tq, int64_t T, int64_t d);
+
+/*
+ * csa_backward -- gradients of the causal forward (eq. (10)-(11)) for training, the use the
+ * pages' experiments make of the method (Experiments; trainable k_0, v_0 under Analysis of
+ * the Result).  The pages print no backward; this is the plain derivative of eq. (10)-(11)
+ * for the loss sum_t dO_t . o_t:
+ *
+ *     dS_{t,i} = P_{t,i} (dO_t . v_i - dO_t . o_t) + G_{(i-1,i)} - G_{(i,i+1)},
+ *     G_{(i,i+1)} = (dO_t . v_i - dO_t . v_{i+1}) / Z_t * integral_0^1 s (1-s) e^{(1-s) a_i + s a_{i+1}} ds,
+ *
+ * with P_{t,i} = e^{a_{t,i} + b_{t,i}} / Z_t, edges only between consecutive positions 0..t,
+ * and dq_t = sum_i dS_{t,i} k_i, dk_i = sum_t dS_{t,i} q_t, dv_i = sum_t P_{t,i} dO_t.
+ *
+ *   q, k, v    device, [B, H, T, d] bf16, 16-byte aligned (the forward's inputs).
+ *   k0, v0     device, [B, H, d] bf16, 16-byte aligned, or NULL (zeros), as in csa_forward.
+ *   o, lse     device: the forward's out [B, H, T, d] bf16 and lse [B, H, T] float32 (4-byte
+ *              aligned) for these inputs; P is recomputed from lse.
+ *   dout       device, [B, H, T, d] bf16: dLoss/do.
+ *   dq, dk, dv device, [B, H, T, d] bf16 outputs (fully written).
+ *   dk0, dv0   device, [B, H, d] bf16 outputs (16-byte aligned), or NULL to skip; written even
+ *              when k0 / v0 is NULL (the gradient at the zero vector).
+ *   workspace  device, 16-byte aligned, at least csa_backward_workspace_bytes(B, H, T, d)
+ *              bytes, caller-owned scratch (no initialisation needed); calls sharing it must be
+ *              ordered on one stream.
+ *   d          64 or 128 (16 returns CSA_ERR_UNSUPPORTED); dtype must be CSA_BF16.
+ *   stream     hipStream_t or NULL.
+ *
+ * Gradients are accumulated in float32 and rounded once to bf16; the bf16 operands of the
+ * matrix products (P, dS) are rounded like the forward's P.  Returns CSA_OK, or
+ * CSA_ERR_INVALID_ARG (null required pointer, sizes, alignment, a short workspace, or any
+ * output overlapping another output or an input), CSA_ERR_UNSUPPORTED, CSA_ERR_HIP; nothing is
+ * launched on an error.  Up to four kernel launches on `stream`.
+ */
+int csa_backward(const void* q, const void* k, const void* v, const void* k0, const void* v0,
+                 const void* o, const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                 void* dk0, void* dv0, void* workspace, int64_t workspace_bytes, int64_t B, int64_t H,
+                 int64_t T, int64_t d, int dtype, void* stream);
+
+/* The argument validation of csa_backward alone (no HIP call). */
+int csa_backward_check(const void* q, const void* k, const void* v, const void* k0, const void* v0,
+                       const void* o, const float* lse, const void* dout, const void* dq,
+                       const void* dk, const void* dv, const void* dk0, const void* dv0,
+                       const void* workspace, int64_t workspace_bytes, int64_t B, int64_t H, int64_t T,
+                       int64_t d, int dtype);
+
+/* Workspace bytes csa_backward needs for these sizes, or -1 if the sizes are invalid. */
+int64_t csa_backward_workspace_bytes(int64_t B, int64_t H, int64_t T, int64_t d);
 
 /* Static, NUL-terminated description of a return code. */
 const char* csa_status_string(int status);

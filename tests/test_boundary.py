@@ -36,6 +36,7 @@ def test_exports_every_declared_symbol(lib, header):
 def test_header_declares_the_entry_points():
     assert {"csa_forward", "csa_forward_check", "csa_forward_first_order", "csa_forward_first_order_check",
             "csa_decode", "csa_decode_check", "csa_decode_workspace_bytes",
+            "csa_backward", "csa_backward_check", "csa_backward_workspace_bytes",
             "csa_status_string"} <= set(csa.header_functions("csa.h"))
     assert {"std_fwd", "std_fwd_check"} <= set(csa.header_functions("csa_bench.h"))
 
@@ -189,6 +190,60 @@ def test_decode_check_rules():
                               a["B"], a["H"], 9, a["T"], a["d"], a["dtype"]) == INV
 
 
+def _bargs(**kw):
+    big = 2 * 3 * 100 * 64 * 2  # B*H*T*d bf16 bytes of the default sizes (< 1 MB)
+    a = dict(q=A, k=A + 1 * MB, v=A + 2 * MB, k0=None, v0=None, o=A + 3 * MB, lse=A + 4 * MB, dout=A + 5 * MB,
+             dq=A + 6 * MB, dk=A + 7 * MB, dv=A + 8 * MB, dk0=A + 9 * MB, dv0=A + 10 * MB, ws=A + 11 * MB,
+             wsb=1 << 20, B=2, H=3, T=100, d=64, dtype=csa.CSA_BF16)
+    assert big < MB
+    a.update(kw)
+    return a
+
+
+def _bcheck(**kw):
+    a = _bargs(**kw)
+    return csa.csa_backward_check(a["q"], a["k"], a["v"], a["k0"], a["v0"], a["o"], a["lse"], a["dout"],
+                                  a["dq"], a["dk"], a["dv"], a["dk0"], a["dv0"], a["ws"], a["wsb"],
+                                  a["B"], a["H"], a["T"], a["d"], a["dtype"])
+
+
+def test_backward_workspace_size():
+    # 512 zero bytes, then D_t, mu_t, dS_{t,0}, P_{t,0} as float32 per (b, h, t)
+    assert csa.csa_backward_workspace_bytes(2, 3, 100, 64) == 512 + 16 * 2 * 3 * 100
+    assert csa.csa_backward_workspace_bytes(4, 16, 4096, 128) == 512 + 16 * 4 * 16 * 4096
+    for bad in (dict(d=16), dict(d=32), dict(B=0), dict(T=0), dict(H=-1)):
+        a = dict(B=1, H=1, T=100, d=64)
+        a.update(bad)
+        assert csa.csa_backward_workspace_bytes(a["B"], a["H"], a["T"], a["d"]) == -1
+
+
+def test_backward_check_rules():
+    assert _bcheck() == OK
+    assert _bcheck(d=128) == OK
+    assert _bcheck(dk0=None, dv0=None) == OK
+    assert _bcheck(k0=A + 12 * MB, v0=A + 13 * MB) == OK
+    assert _bcheck(dtype=csa.CSA_F32) == UNS   # bf16 kernels only
+    assert _bcheck(d=16) == UNS
+    assert _bcheck(d=96) == UNS
+    for field in ("q", "k", "v", "o", "lse", "dout", "dq", "dk", "dv", "ws"):
+        assert _bcheck(**{field: None}) == INV, field
+    for bad in (dict(wsb=512 + 16 * 600 - 1),           # one byte short
+                dict(B=0), dict(T=0),
+                dict(q=A + 8), dict(dq=A + 6 * MB + 8), dict(ws=A + 11 * MB + 4), dict(lse=A + 4 * MB + 2),
+                dict(dk0=A + 9 * MB + 2),
+                dict(dq=A + 64),                          # dq inside q
+                dict(dk=A + 6 * MB + 16),                 # dk inside dq
+                dict(ws=A + 5 * MB + 4096),               # workspace inside dout
+                dict(dv0=A + 9 * MB + 16),                # dv0 inside dk0
+                dict(dk0=A + 4 * MB)):                    # dk0 inside lse
+        assert _bcheck(**bad) == INV, bad
+    # the launching entry point rejects the same calls before any HIP call
+    a = _bargs(dtype=csa.CSA_F32)
+    assert csa.csa_backward_raw(a["q"], a["k"], a["v"], None, None, a["o"], a["lse"], a["dout"], a["dq"], a["dk"],
+                                a["dv"], None, None, a["ws"], a["wsb"], a["B"], a["H"], a["T"], a["d"],
+                                a["dtype"]) == UNS
+
+
 def test_status_strings():
     for s in (OK, INV, UNS, csa.CSA_ERR_HIP, 99):
         assert isinstance(csa.status_string(s), str) and csa.status_string(s)
@@ -202,3 +257,5 @@ def test_python_binding_refuses_cpu_tensors():
         csa.csa_forward(q, q, q)
     with pytest.raises(ValueError):
         csa.std_fwd(q, q, q)
+    with pytest.raises(ValueError):
+        csa.csa_backward(q, q, q, q, torch.zeros(1, 1, 4), q)

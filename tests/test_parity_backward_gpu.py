@@ -1,0 +1,189 @@
+"""GPU parity of the backward pass (csa_backward, bf16) against the float64 gradient
+reference (oracle.backward, pinned to finite differences of the defining integral).
+
+The forward runs on the GPU (csa_forward) to give o and lse, as in training; the
+reference differentiates the float64 forward of the same bf16 inputs.
+
+Tolerance.  The pages fix a bar for o and lse only (max abs error 2e-2 for bf16).  For a
+gradient G the same bar is applied to G scaled to unit size:
+    max |G - G_ref| <= 2e-2 * max(1, max |G_ref|).
+Derivation: the kernels round P and dS to bf16 before the matrix products (relative
+2^-9) and round each gradient once to bf16; a float64 emulation of exactly those
+roundings gives 3e-3 .. 6e-3 on this measure for logits of standard deviation 1 to 12,
+so 2e-2 leaves a factor of three or more.
+"""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import continuous_softmax_attention_amd as csa
+from oracle import csa_backward_reference
+from workloads import make_grad_output, make_inputs
+
+pytestmark = pytest.mark.gpu
+DEV = torch.device("cuda:0")
+TOL = 2e-2
+NAMES = ("dq", "dk", "dv", "dk0", "dv0")
+
+
+def _gpu(*ts):
+    return [None if t is None else t.to(DEV) for t in ts]
+
+
+def _np(t):
+    return None if t is None else t.float().cpu().double().numpy()
+
+
+def _run(q, k, v, k0, v0, do, sink_grads=True):
+    qg, kg, vg, k0g, v0g, dog = _gpu(q, k, v, k0, v0, do)
+    o, lse = csa.csa_forward(qg, kg, vg, k0g, v0g)
+    grads = csa.csa_backward(qg, kg, vg, o, lse, dog, k0g, v0g, sink_grads=sink_grads)
+    torch.cuda.synchronize()
+    return [_np(g) for g in grads]
+
+
+def _nerr(got, ref):
+    return float(np.abs(got - ref).max()) / max(1.0, float(np.abs(ref).max()))
+
+
+def _compare(tag, got, ref, names=NAMES):
+    errs = {}
+    for name, g, r in zip(names, got, ref):
+        if g is None:
+            continue
+        assert np.all(np.isfinite(g)), f"{tag}: non-finite {name}"
+        errs[name] = _nerr(g, r)
+    print(f"[parity backward] {tag}: " + "  ".join(f"{n} {e:.2e}" for n, e in errs.items()), flush=True)
+    for name, e in errs.items():
+        assert e <= TOL, (tag, name, e)
+    return errs
+
+
+def _random_case(B, H, T, d, seed, q_mult=1.0, sink=True):
+    g = torch.Generator().manual_seed(seed)
+    q = torch.randn(B, H, T, d, generator=g) * (q_mult / math.sqrt(d))
+    k = torch.randn(B, H, T, d, generator=g)
+    v = torch.randn(B, H, T, d, generator=g)
+    k0 = torch.randn(B, H, d, generator=g) if sink else None
+    v0 = torch.randn(B, H, d, generator=g) if sink else None
+    cast = (lambda t: None if t is None else t.bfloat16())
+    do = make_grad_output((B, H, T, d), torch.bfloat16, seed)
+    return cast(q), cast(k), cast(v), cast(k0), cast(v0), do
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("T", [1, 2, 3, 17, 63, 64, 65, 127, 128, 129, 200, 257])
+def test_edge_shapes_with_random_sink(T, d):
+    print(f"[backward] T={T} d={d}", flush=True)
+    q, k, v, k0, v0, do = _random_case(1, 2, T, d, seed=9100 * T + d)
+    got = _run(q, k, v, k0, v0, do)
+    ref = csa_backward_reference(q, k, v, do, k0, v0)
+    _compare(f"T{T} d{d}", got, ref)
+
+
+def test_many_heads_no_sink():
+    # k0 = v0 = 0: dk0, dv0 are the gradient at the zero vector
+    print("[backward] B2 H3 T300 d128 no sink", flush=True)
+    q, k, v, _, _, do = _random_case(2, 3, 300, 128, seed=31, sink=False)
+    got = _run(q, k, v, None, None, do)
+    ref = csa_backward_reference(q, k, v, do)
+    _compare("B2 H3 T300 no sink", got, ref)
+
+
+@pytest.mark.parametrize("q_mult", [4.0, 8.0, 12.0])
+def test_large_logits_copied_sink(q_mult):
+    # k0 = k_1: the first edge has an exactly zero logit difference (Taylor branches)
+    print(f"[backward] large logits x{q_mult}", flush=True)
+    q, k, v, _, _, do = _random_case(1, 3, 333, 128, seed=83, q_mult=q_mult, sink=False)
+    k0, v0 = k[:, :, 0].clone(), v[:, :, 0].clone()
+    got = _run(q, k, v, k0, v0, do)
+    ref = csa_backward_reference(q, k, v, do, k0, v0)
+    _compare(f"large logits x{q_mult}", got, ref)
+
+
+def test_long_sequence_d64():
+    print("[backward] B1 H1 T1000 d64", flush=True)
+    q, k, v, k0, v0, do = _random_case(1, 1, 1000, 64, seed=47)
+    got = _run(q, k, v, k0, v0, do)
+    ref = csa_backward_reference(q, k, v, do, k0, v0)
+    _compare("T1000 d64", got, ref)
+
+
+def test_sink_grads_optional_and_deterministic():
+    print("[backward] sink grads off / determinism", flush=True)
+    q, k, v, k0, v0, do = _random_case(1, 2, 190, 128, seed=5)
+    a = _run(q, k, v, k0, v0, do)
+    b = _run(q, k, v, k0, v0, do, sink_grads=False)
+    assert b[3] is None and b[4] is None
+    for x, y in zip(a[:3], b[:3]):
+        assert np.array_equal(x, y)  # no atomics: identical bits on every call
+
+
+def test_workspace_reuse_with_smaller_second_call():
+    print("[backward] workspace reuse", flush=True)
+    ws = torch.empty(csa.csa_backward_workspace_bytes(1, 2, 300, 64), dtype=torch.uint8, device=DEV)
+    for T, seed in ((300, 1), (77, 2)):
+        q, k, v, k0, v0, do = _random_case(1, 2, T, 64, seed=seed)
+        qg, kg, vg, k0g, v0g, dog = _gpu(q, k, v, k0, v0, do)
+        o, lse = csa.csa_forward(qg, kg, vg, k0g, v0g)
+        got = [_np(g) for g in csa.csa_backward(qg, kg, vg, o, lse, dog, k0g, v0g, workspace=ws)]
+        torch.cuda.synchronize()
+        _compare(f"workspace reuse T{T}", got, csa_backward_reference(q, k, v, do, k0, v0))
+
+
+def test_rejects_unsupported_before_launch():
+    q = torch.zeros(1, 1, 8, 64, device=DEV)
+    lse = torch.zeros(1, 1, 8, device=DEV)
+    with pytest.raises(csa.CsaError) as e:  # float32: the backward kernels are bf16
+        csa.csa_backward(q, q, q, q, lse, q)
+    assert e.value.status == csa.CSA_ERR_UNSUPPORTED
+    qb = torch.zeros(1, 1, 8, 16, device=DEV, dtype=torch.bfloat16)
+    with pytest.raises(csa.CsaError) as e:
+        csa.csa_backward(qb, qb, qb, qb, lse, qb)
+    assert e.value.status == csa.CSA_ERR_UNSUPPORTED
+
+
+def _check_shift_symmetries(tag, do, got):
+    """sum over positions of dv = sum_t dO_t; sum over positions of dk = 0 (no lse gradient).
+
+    Each residual, per (head, column), is divided by the L2 norm of the summed gradient
+    column.  In exact arithmetic it is zero; with bf16 o (which enters D_t = dO_t . o_t)
+    and bf16-rounded P, dS and outputs it is a sum of T independent rounding terms (one per
+    query), so its maximum over the ~8k (head, column) samples of a workload sits several
+    standard deviations out: it measured 1.1e-2 .. 1.8e-2 on the two workloads.  The bar:
+    RMS over all heads and columns <= 1e-2 and maximum <= 5e-2.
+    """
+    dq, dk, dv, dk0, dv0 = got
+    sv = dv.sum(axis=2) + dv0 - do.float().double().numpy().sum(axis=2)
+    sk = dk.sum(axis=2) + dk0
+    nv = np.sqrt((dv ** 2).sum(axis=2) + dv0 ** 2)
+    nk = np.sqrt((dk ** 2).sum(axis=2) + dk0 ** 2)
+    rv, rk = np.abs(sv) / np.maximum(nv, 1.0), np.abs(sk) / np.maximum(nk, 1.0)
+    stats = [float(np.sqrt((r ** 2).mean())) for r in (rv, rk)] + [float(r.max()) for r in (rv, rk)]
+    print(f"[parity backward] {tag} shift symmetries: rms dv {stats[0]:.2e} dk {stats[1]:.2e}  "
+          f"max dv {stats[2]:.2e} dk {stats[3]:.2e}", flush=True)
+    assert stats[0] <= 1e-2 and stats[1] <= 1e-2
+    assert stats[2] <= 5e-2 and stats[3] <= 5e-2
+
+
+@pytest.mark.parametrize("name,heads", [("lm", [(0, 0), (3, 15)]), ("stress", [(1, 7)])])
+def test_workload_full_size_sampled_heads(name, heads):
+    """The workload at full size, in the launch configuration of the bench: every head
+    finite and checked against the shift symmetries, sampled heads against the reference."""
+    print(f"[backward] workload {name} full size", flush=True)
+    q, k, v, k0, v0 = make_inputs(name)
+    w_seed = {"lm": 3, "stress": 5}[name]
+    do = make_grad_output(q.shape, q.dtype, w_seed)
+    got = _run(q, k, v, k0, v0, do)
+    B, H = q.shape[:2]
+    if k0 is None:
+        k0 = torch.zeros(B, H, q.shape[-1], dtype=q.dtype)
+        v0 = torch.zeros(B, H, q.shape[-1], dtype=q.dtype)
+    _check_shift_symmetries(name, do, got)
+    for b, h in heads:
+        sl = slice(b, b + 1), slice(h, h + 1)
+        ref = csa_backward_reference(q[sl], k[sl], v[sl], do[sl], k0[sl], v0[sl])
+        _compare(f"{name} head ({b},{h})", [g[sl] for g in got], ref)

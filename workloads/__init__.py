@@ -32,6 +32,10 @@ decode       6     16, 8, 1, 8192, 128            bf16   q *= 1/sqrt(d); zeros
 decode_spec  7     16, 8, 8, 8192, 128            bf16   q *= 1/sqrt(d); zeros
 ===========  ====  =============================  =====  ===========================
 
+Backward pass: the same (q, k, v, k_0, v_0) as the workload, plus an upstream
+gradient dO ~ N(0, 1) of the output's shape drawn from its own generator seeded
+``seed + 1000`` (``make_grad_output``).
+
 The pages fix no shapes; their experiments are language-model training runs
 with rotary embeddings, which ``lm`` stands in for.  "All zeros" and "copy
 the first key/value" are two of the k_0/v_0 choices listed under Analysis of
@@ -199,6 +203,13 @@ def make_inputs(w: Workload | str, *, B=None, H=None, T=None, d=None, dtype=None
     else:
         k0 = v0 = None
     return q, k, v, k0, v0
+
+
+def make_grad_output(shape, dtype, seed: int):
+    """Upstream gradient dO for the backward pass: N(0, 1) of ``shape`` from its own
+    generator (``seed + 1000``), cast once to ``dtype`` (a torch dtype)."""
+    g = torch.Generator("cpu").manual_seed(seed + 1000)
+    return torch.randn(tuple(shape), generator=g, dtype=torch.float32).to(dtype)
 
 
 def sample_rows(T: int, seed: int, n_random: int = 48, tile: int = 64, n_edges: int = 4):

@@ -12,7 +12,10 @@ same tiling (std_fwd) runs on the same inputs for the ratio, and so does the
 first-order variant (csa_forward_first_order, b as the second difference of the
 logits) -- the same kernel without the exact correction weights.  The ``decode``
 object times csa_decode (a few new queries against a key/value cache, bound by HBM
-bandwidth) on the decode workloads.
+bandwidth) on the decode workloads, and ``backward`` times csa_backward (the gradients
+dq, dk, dv, dk0, dv0 from the forward's o and lse and a seeded dO) on the same workload,
+counting 2.5 times the forward's FLOP (five matrix products of the forward's size against
+its two: S recomputed, dP, dV, dK, dQ).
 
 Prints ONE JSON line.  `cpu_baseline` times the float64 CPU reference on a
 bounded sample of query rows of the same workload (process pool over host
@@ -185,8 +188,9 @@ def decode_legs(steps, warmup):
 
 def counters_mode(w, q, k, v, k0, v0):
     """One launch of each kernel plus a 256 MiB device-to-device copy whose HBM bytes
-    are known (256 MiB read + 256 MiB written), to scale FETCH_SIZE/WRITE_SIZE; then one
-    csa_decode call on the decode workload."""
+    are known (256 MiB read + 256 MiB written), to scale FETCH_SIZE/WRITE_SIZE; then (bf16
+    workloads) a forward and one csa_backward call, and one csa_decode call on the decode
+    workload."""
     import torch
 
     import continuous_softmax_attention_amd as csa
@@ -207,6 +211,14 @@ def counters_mode(w, q, k, v, k0, v0):
     if w.dtype == "bf16":
         csa.csa_forward_first_order(qd, kd, vd, k0d, v0d)
         torch.cuda.synchronize()
+        from workloads import make_grad_output
+
+        o, lse = csa.csa_forward(qd, kd, vd, k0d, v0d)
+        dod = make_grad_output(q.shape, q.dtype, w.seed).to(dev)
+        torch.cuda.synchronize()
+        csa.csa_backward(qd, kd, vd, o, lse, dod, k0d, v0d)
+        torch.cuda.synchronize()
+        del o, lse, dod
     del qd, kd, vd
     from workloads import make_decode_inputs
 
@@ -227,6 +239,7 @@ def main():
     ap.add_argument("--no-std", action="store_true")
     ap.add_argument("--no-first-order", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-backward", action="store_true")
     ap.add_argument("--counters", action="store_true",
                     help="for rocprofv3 --pmc passes: one plain device copy of 256 MiB (counter "
                          "calibration), one csa_forward and one std_fwd launch, then exit")
@@ -318,6 +331,24 @@ def main():
         res["first_order"] = {"value": round(f_tflops, 2), "unit": "TFLOP/s", "kernel_ms": round(f_avg, 4),
                               "pct_peak": round(100.0 * f_tflops / peak, 2),
                               "exact_over_first_order": round(tflops / f_tflops, 4)}
+    if not args.no_backward and w.dtype == "bf16":
+        from workloads import make_grad_output
+
+        dod = make_grad_output(q.shape, q.dtype, w.seed).to(dev)
+        grads = [torch.empty_like(qd) for _ in range(3)]
+        bws = torch.empty(csa.csa_backward_workspace_bytes(w.B, w.H, w.T, w.d), dtype=torch.uint8, device=dev)
+        csa.csa_forward(qd, kd, vd, k0d, v0d, out=out, lse=lse, stream=stream)
+
+        def bwd_step():
+            csa.csa_backward(qd, kd, vd, out, lse, dod, k0d, v0d, dq=grads[0], dk=grads[1], dv=grads[2],
+                             workspace=bws, stream=stream)
+
+        b_avg, b_min, _ = time_kernel(bwd_step, args.steps, args.warmup, stream)
+        b_tflops = 2.5 * flop / (b_avg * 1e-3) / 1e12
+        res["backward"] = {"value": round(b_tflops, 2), "unit": "TFLOP/s", "kernel_ms": round(b_avg, 4),
+                           "min_ms": round(b_min, 4), "pct_peak": round(100.0 * b_tflops / peak, 2),
+                           "flop": "2.5 x forward", "fwd_plus_bwd_ms": round(avg_ms + b_avg, 4)}
+        del dod, grads, bws
     if not args.no_decode:
         res["decode"] = decode_legs(args.steps, args.warmup)
     if cpu is not None:

@@ -34,7 +34,8 @@
 //             (16 consecutive keys of one query, neighbours across lane groups by
 //             ds_bpermute); dQ^T += K^T dS^T with K^T through transposed LDS reads.  Also
 //             writes dS and P of position 0 per query.
-//   bwd_sink  dk_0 = sum_t dS_{t,0} q_t, dv_0 = sum_t P_{t,0} dO_t (skipped when both are null).
+//   bwd_sink  dk_0 = sum_t dS_{t,0} q_t, dv_0 = sum_t P_{t,0} dO_t: partial sums over 16
+//             row ranges per (b, h), then their fixed-order sum (skipped when both are null).
 //   bwd_dkdv  one work-group per 64 key rows, looping over 128-row query tiles: the same
 //             S^T, dP^T, P and dS per wave; P and dS (bf16) go through LDS so that
 //             dV^T += dO^T P and dK^T += Q^T dS contract over queries on MFMAs.
@@ -62,14 +63,14 @@ struct BwdParams {
   void* dv;
   void* dk0;  // may be null (not written)
   void* dv0;  // may be null (not written)
-  char* ws;   // workspace, bwd_workspace_bytes()
+  char* ws;   // workspace of csa_backward_workspace_bytes() bytes
   int B, H, T;
 };
 
 // Workspace: 512 zero bytes (two rows of up to 128 bf16), then four float arrays of
-// B*H*T: D_t, mu_t, dS_{t,0}, P_{t,0}.
+// B*H*T: D_t, mu_t, dS_{t,0}, P_{t,0}; then the float partial sums of dk_0 and dv_0,
+// B*H x 16 chunks x 2 x 128 (sized for d = 128 whatever d is).
 constexpr int kBwdZeroBytes = 512;
-inline int64_t bwd_workspace_bytes(int64_t BH, int64_t T) { return kBwdZeroBytes + 16 * BH * T; }
 
 struct BwdWs {
   const char* zero;
@@ -77,11 +78,12 @@ struct BwdWs {
   float* mu;
   float* ds0;
   float* p0;
+  float* sink;
 };
 __device__ __forceinline__ BwdWs bwd_ws(char* ws, int BH, int T) {
   const size_t n = (size_t)BH * (size_t)T;
   float* f = (float*)(ws + kBwdZeroBytes);
-  return {ws, f, f + n, f + 2 * n, f + 3 * n};
+  return {ws, f, f + n, f + 2 * n, f + 3 * n, f + 4 * n};
 }
 
 constexpr float kMuShift = -1.0575327458897954f;  // 2 log2(ln 2)
@@ -472,19 +474,26 @@ __global__ void __launch_bounds__(512, 2) bwd_dq_kernel(BwdParams p) {
   }
 }
 
-// dk_0 = sum_t dS_{t,0} q_t and dv_0 = sum_t P_{t,0} dO_t: one work-group per (b, h)
+// dk_0 = sum_t dS_{t,0} q_t and dv_0 = sum_t P_{t,0} dO_t in two passes: kSinkChunks
+// work-groups per (b, h) each sum a contiguous range of query rows into float32 partials
+// in the workspace; one work-group per (b, h) adds the partials (fixed order: the result
+// does not depend on scheduling) and rounds once.
+constexpr int kSinkChunks = 16;
+
 template <int D>
-__global__ void __launch_bounds__(256) bwd_sink_kernel(BwdParams p) {
+__global__ void __launch_bounds__(256) bwd_sink_partial_kernel(BwdParams p) {
   constexpr int CH = D / 8;
   constexpr int NPH = 256 / CH;  // row phases
   __shared__ float red[2][NPH][D];
   const int BH = p.B * p.H, Tn = p.T;
   const BwdWs ws = bwd_ws(p.ws, BH, Tn);
-  const int bh = blockIdx.x;
+  const int bh = blockIdx.x / kSinkChunks, chunk = blockIdx.x % kSinkChunks;
+  const int rows = (Tn + kSinkChunks - 1) / kSinkChunks;
+  const int t0 = chunk * rows, t1 = min(Tn, t0 + rows);
   const int c = threadIdx.x % CH, ph = threadIdx.x / CH;
   const size_t head = (size_t)bh * (size_t)Tn * D;
   float ak[8] = {}, av[8] = {};
-  for (int t = ph; t < Tn; t += NPH) {
+  for (int t = t0 + ph; t < t1; t += NPH) {
     const float a = ws.ds0[(size_t)bh * Tn + t];
     const float b = ws.p0[(size_t)bh * Tn + t];
     const bf16x8 qv = *(const bf16x8*)((const bf16*)p.q + head + (size_t)t * D + 8 * c);
@@ -505,6 +514,19 @@ __global__ void __launch_bounds__(256) bwd_sink_kernel(BwdParams p) {
     const int which = threadIdx.x / D, d = threadIdx.x % D;
     float sum = 0.0f;
     for (int i = 0; i < NPH; ++i) sum += red[which][i][d];
+    ws.sink[((size_t)bh * kSinkChunks + chunk) * 2 * D + which * D + d] = sum;
+  }
+}
+
+template <int D>
+__global__ void __launch_bounds__(256) bwd_sink_final_kernel(BwdParams p) {
+  const int BH = p.B * p.H;
+  const BwdWs ws = bwd_ws(p.ws, BH, p.T);
+  const int bh = blockIdx.x;
+  if (threadIdx.x < 2 * D) {
+    const int which = threadIdx.x / D, d = threadIdx.x % D;
+    float sum = 0.0f;
+    for (int i = 0; i < kSinkChunks; ++i) sum += ws.sink[((size_t)bh * kSinkChunks + i) * 2 * D + which * D + d];
     bf16* dst = (bf16*)(which == 0 ? p.dk0 : p.dv0);
     if (dst) dst[(size_t)bh * D + d] = (bf16)sum;
   }
@@ -664,8 +686,10 @@ inline hipError_t launch_backward(const BwdParams& prm, hipStream_t stream) {
   hipLaunchKernelGGL((bwd_pre_kernel<D>), dim3((unsigned)((rows + rpb - 1) / rpb)), dim3(256), 0, stream, prm);
   const int nqb = (prm.T + kBlockRows - 1) / kBlockRows;
   hipLaunchKernelGGL((bwd_dq_kernel<D>), dim3((unsigned)(nqb * BH)), dim3(512), 0, stream, prm);
-  if (prm.dk0 != nullptr || prm.dv0 != nullptr)
-    hipLaunchKernelGGL((bwd_sink_kernel<D>), dim3((unsigned)BH), dim3(256), 0, stream, prm);
+  if (prm.dk0 != nullptr || prm.dv0 != nullptr) {
+    hipLaunchKernelGGL((bwd_sink_partial_kernel<D>), dim3((unsigned)(BH * kSinkChunks)), dim3(256), 0, stream, prm);
+    hipLaunchKernelGGL((bwd_sink_final_kernel<D>), dim3((unsigned)BH), dim3(256), 0, stream, prm);
+  }
   const int nkb = (prm.T + kTile - 1) / kTile;
   hipLaunchKernelGGL((bwd_dkdv_kernel<D>), dim3((unsigned)(nkb * BH)), dim3(512), 0, stream, prm);
   return hipGetLastError();

@@ -105,7 +105,7 @@ inline int64_t backward_workspace_bytes(int64_t B, int64_t H, int64_t T, int64_t
   if (d != 64 && d != 128) return -1;
   const int64_t kMax32 = (int64_t(1) << 31) - 1;
   if (T > kMax32 / 2 || B > kMax32 || H > kMax32 || B * H > kMax32 / T) return -1;  // B*H*T rows < 2^31
-  return 512 + 16 * B * H * T;
+  return 512 + 16 * B * H * T + B * H * 16 * 2 * 128 * 4;  // see bwd16.hpp for the layout
 }
 
 inline int validate_backward(const void* q, const void* k, const void* v, const void* k0, const void* v0,

@@ -175,7 +175,7 @@ int64_t csa_decode_workspace_bytes(int64_t B, int64_t H, int64_t Tq, int64_t T, 
  * matrix products (P, dS) are rounded like the forward's P.  Returns CSA_OK, or
  * CSA_ERR_INVALID_ARG (null required pointer, sizes, alignment, a short workspace, or any
  * output overlapping another output or an input), CSA_ERR_UNSUPPORTED, CSA_ERR_HIP; nothing is
- * launched on an error.  Up to four kernel launches on `stream`.
+ * launched on an error.  Up to five kernel launches on `stream`.
  */
 int csa_backward(const void* q, const void* k, const void* v, const void* k0, const void* v0,
                  const void* o, const float* lse, const void* dout, void* dq, void* dk, void* dv,

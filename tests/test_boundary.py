@@ -208,9 +208,10 @@ def _bcheck(**kw):
 
 
 def test_backward_workspace_size():
-    # 512 zero bytes, then D_t, mu_t, dS_{t,0}, P_{t,0} as float32 per (b, h, t)
-    assert csa.csa_backward_workspace_bytes(2, 3, 100, 64) == 512 + 16 * 2 * 3 * 100
-    assert csa.csa_backward_workspace_bytes(4, 16, 4096, 128) == 512 + 16 * 4 * 16 * 4096
+    # 512 zero bytes, then D_t, mu_t, dS_{t,0}, P_{t,0} as float32 per (b, h, t), then
+    # 16 partial sums of dk_0 and dv_0 (2 x 128 float32) per (b, h)
+    assert csa.csa_backward_workspace_bytes(2, 3, 100, 64) == 512 + 16 * 2 * 3 * 100 + 2 * 3 * 16 * 1024
+    assert csa.csa_backward_workspace_bytes(4, 16, 4096, 128) == 512 + 16 * 4 * 16 * 4096 + 64 * 16 * 1024
     for bad in (dict(d=16), dict(d=32), dict(B=0), dict(T=0), dict(H=-1)):
         a = dict(B=1, H=1, T=100, d=64)
         a.update(bad)
@@ -227,7 +228,7 @@ def test_backward_check_rules():
     assert _bcheck(d=96) == UNS
     for field in ("q", "k", "v", "o", "lse", "dout", "dq", "dk", "dv", "ws"):
         assert _bcheck(**{field: None}) == INV, field
-    for bad in (dict(wsb=512 + 16 * 600 - 1),           # one byte short
+    for bad in (dict(wsb=512 + 16 * 600 + 6 * 16 * 1024 - 1),   # one byte short
                 dict(B=0), dict(T=0),
                 dict(q=A + 8), dict(dq=A + 6 * MB + 8), dict(ws=A + 11 * MB + 4), dict(lse=A + 4 * MB + 2),
                 dict(dk0=A + 9 * MB + 2),

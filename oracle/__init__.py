@@ -27,3 +27,4 @@ from .csa import (  # noqa: F401
 )
 from .first_order import csa1_reference, csa1_row  # noqa: F401
 from .backward import csa_backward_reference, csa_backward_row, dphi1, dphi2  # noqa: F401
+from .half_interval import csa_half_reference, csa_half_row, seg_integrals  # noqa: F401

@@ -334,3 +334,97 @@ def dev_grad_trapezoid(ref_bwd, seed=13, T=7):
         expect[: t + 1] += np.outer(w / t, do[0, 0, r])
     got = np.concatenate([dv0[0, 0][None], dv_[0, 0]], axis=0)
     return float(np.abs(got - expect).max())
+
+
+# ---------------------------------------------------------------- interval [1/2, t + 1/2]
+
+def quadrature_half_row(q_t, k_hat, v_hat, t):
+    """(o_t, lse_t) integrating eq. (2) over [1/2, t + 1/2] with the interpolation of eq. (3).
+
+    k_hat, v_hat hold positions 0..t+1.  Each covered piece of a unit segment is integrated
+    with the 48-point Gauss-Legendre rule on 4 sub-intervals, as ``quadrature_row``.
+    """
+    pieces = [(1, 0.5, 1.0)] + [(i, 0.0, 1.0) for i in range(2, t + 1)] + [(t + 1, 0.0, 0.5)]
+    terms = []
+    for i, lo, hi in pieces:
+        for sub in range(4):
+            a, b = lo + (hi - lo) * sub / 4, lo + (hi - lo) * (sub + 1) / 4
+            s_local = a + (b - a) * _GL_S
+            w = _GL_W01 * (b - a)
+            k_s = (1.0 - s_local)[:, None] * k_hat[i - 1] + s_local[:, None] * k_hat[i]
+            v_s = (1.0 - s_local)[:, None] * v_hat[i - 1] + s_local[:, None] * v_hat[i]
+            terms.append((k_s @ q_t, w, v_s))
+    shift = max(float(x.max()) for x, _, _ in terms)
+    num = np.zeros(v_hat.shape[1])
+    den = 0.0
+    for logits, w, v_s in terms:
+        e = np.exp(logits - shift) * w
+        den += e.sum()
+        num += e @ v_s
+    return num / den, shift + math.log(den)
+
+
+def _half_hat(q, k, v, k0, v0):
+    """Positions 0..T+1 with position T+1 repeating position T (the last query's convention)."""
+    qq, kh, vh = hat(q, k, v, k0, v0)
+    return qq, np.concatenate([kh, kh[-1:]]), np.concatenate([vh, vh[-1:]])
+
+
+def dev_half_vs_quadrature(ref, seed=0, scale=1.0):
+    """Max |reference - quadrature over [1/2, t + 1/2]| over all rows (incl. the last)."""
+    q, k, v, k0, v0 = random_case(seed, scale=scale)
+    o, lse = ref(q, k, v, k0, v0)
+    qq, kh, vh = _half_hat(q, k, v, k0, v0)
+    worst = 0.0
+    for r in range(q.shape[2]):
+        oq, lq = quadrature_half_row(qq[r], kh, vh, r + 1)
+        worst = max(worst, float(np.abs(o[0, 0, r] - oq).max()), abs(float(lse[0, 0, r]) - lq))
+    return worst
+
+
+def dev_half_trapezoid(ref, seed=2, T=7):
+    """Equal logits (q = 0): o_t is the average of v_s over [1/2, t + 1/2], i.e. weights
+    1/8, 7/8, 1, ..., 1, 7/8, 1/8 on positions 0..t+1 (t = 1: 1/8, 3/4, 1/8); lse = ln t."""
+    _, k, v, k0, v0 = random_case(seed, T=T)
+    q = np.zeros((1, 1, T, k.shape[-1]))
+    o, lse = ref(q, k, v, k0, v0)
+    _, _, vh = _half_hat(q, k, v, k0, v0)
+    worst = 0.0
+    for r in range(T):
+        t = r + 1
+        w = np.ones(t + 2)
+        w[0] = w[t + 1] = 1.0 / 8.0
+        if t == 1:
+            w[1] = 0.75
+        else:
+            w[1] = w[t] = 7.0 / 8.0
+        expect = (w @ vh[: t + 2]) / t
+        worst = max(worst, float(np.abs(o[0, 0, r] - expect).max()), abs(float(lse[0, 0, r]) - math.log(t)))
+    return worst
+
+
+def dev_half_linear_ramp(ref, beta=0.7, T=6):
+    """k_i = i w, v_i = i c (k_0 = v_0 = 0): q.k_s = beta s and v_s = s c on [0, T], so for
+    t < T (position t+1 is a real key)
+    o_t = c [s e^{beta s}/beta - e^{beta s}/beta^2] / [e^{beta s}/beta] over [1/2, t + 1/2],
+    lse_t = ln((e^{beta (t+1/2)} - e^{beta/2})/beta)."""
+    d, dv = 3, 2
+    w = np.array([0.3, -0.2, 0.5])
+    qv = w * (beta / float(w @ w))
+    c = np.array([1.5, -0.25])
+    pos = np.arange(1, T + 1, dtype=np.float64)
+    q = np.broadcast_to(qv, (1, 1, T, d)).copy()
+    k = (pos[:, None] * w[None, :])[None, None]
+    v = (pos[:, None] * c[None, :])[None, None]
+    o, lse = ref(q, k, v, np.zeros((1, 1, d)), np.zeros((1, 1, dv)))
+    worst = 0.0
+    with mp.workdps(40):
+        bb = mp.mpf(beta)
+        for r in range(T - 1):
+            t = r + 1
+            lo, hi = mp.mpf(1) / 2, mp.mpf(t) + mp.mpf(1) / 2
+            den = (mp.exp(bb * hi) - mp.exp(bb * lo)) / bb
+            num = (mp.exp(bb * hi) * (bb * hi - 1) - mp.exp(bb * lo) * (bb * lo - 1)) / (bb * bb)
+            o_exp = c * float(num / den)
+            worst = max(worst, float(np.abs(o[0, 0, r] - o_exp).max()), abs(float(lse[0, 0, r]) - float(mp.log(den))))
+    return worst

@@ -12,6 +12,7 @@ import pytest
 import oracle.backward as oracle_backward
 import oracle.csa as oracle_csa
 import oracle.first_order as oracle_first_order
+import oracle.half_interval as oracle_half
 import pins
 
 MUTATIONS = {
@@ -138,6 +139,45 @@ def test_backward_mutant_is_caught(name):
     ref = _mutant(*MUTATIONS_BWD[name], fn="csa_backward_reference", module=oracle_backward)
     caught = []
     for check, tol in CHECKS_BWD:
+        try:
+            caught.append(not (check(ref) < tol))
+        except Exception:
+            caught.append(True)
+    assert any(caught), f"mutation '{name}' escaped every pin"
+
+
+# ---------------------------------------------------------------- interval [1/2, t + 1/2]
+
+MUTATIONS_HALF = {
+    "left half taken as the whole segment": ("lo = 0.5 if i == 1 else 0.0", "lo = 0.0"),
+    "right half taken as the whole segment": ("hi = 0.5 if i == t + 1 else 1.0", "hi = 1.0"),
+    "right half segment dropped": ("for i in range(1, t + 2):", "for i in range(1, t + 1):"),
+    "halves swapped": ("lo = 0.5 if i == 1 else 0.0", "lo = 0.5 if i == t + 1 else 0.0"),
+    "weights of the two ends swapped": ("num += e * ((f0 - f1) * V[i - 1] + f1 * V[i])",
+                                        "num += e * (f1 * V[i - 1] + (f0 - f1) * V[i])"),
+    "series antiderivative power": ("(hi ** (n + 2) - lo ** (n + 2)) / (n + 2)", "(hi ** (n + 1) - lo ** (n + 1)) / (n + 2)"),
+    "closed form of F1": ("(ehi * (hi * safe - 1.0) - elo * (lo * safe - 1.0))", "(ehi * (hi * safe + 1.0) - elo * (lo * safe + 1.0))"),
+    "last query without the copied position": ("k[b, h, -1:]], axis=0)", "0 * k[b, h, -1:]], axis=0)"),
+}
+
+CHECKS_HALF = [
+    (pins.dev_half_vs_quadrature, 1e-12),
+    (lambda ref: pins.dev_half_vs_quadrature(ref, seed=3, scale=0.05), 1e-12),
+    (pins.dev_half_trapezoid, 1e-14),
+    (pins.dev_half_linear_ramp, 1e-11),
+]
+
+
+def test_unmutated_half_interval_reference_passes_every_check():
+    for check, tol in CHECKS_HALF:
+        assert check(oracle_half.csa_half_reference) < tol
+
+
+@pytest.mark.parametrize("name", sorted(MUTATIONS_HALF))
+def test_half_interval_mutant_is_caught(name):
+    ref = _mutant(*MUTATIONS_HALF[name], fn="csa_half_reference", module=oracle_half)
+    caught = []
+    for check, tol in CHECKS_HALF:
         try:
             caught.append(not (check(ref) < tol))
         except Exception:

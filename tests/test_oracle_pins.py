@@ -17,7 +17,7 @@ import numpy as np
 import pytest
 
 import pins
-from oracle import csa1_reference, csa_backward_reference, csa_reference, dphi1, dphi2, phi1, phi2, std_reference
+from oracle import csa1_reference, csa_backward_reference, csa_half_reference, seg_integrals, csa_reference, dphi1, dphi2, phi1, phi2, std_reference
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 
@@ -233,3 +233,31 @@ def test_dphi_are_the_derivatives_of_phi():
         fd = (f(x + h) - f(x - h)) / (2 * h)
         assert (np.abs(df(x) - fd) / np.maximum(1.0, np.abs(fd))).max() < 1e-8
     assert dphi1(0.0) == 0.5 and abs(float(dphi2(0.0)) - 1.0 / 6.0) < 1e-17
+
+
+# ---------------------------------------------------------------- interval [1/2, t + 1/2]
+
+@pytest.mark.parametrize("seed,scale", [(0, 1.0), (3, 0.05), (4, 3.0)])
+def test_half_interval_against_quadrature_of_definition(seed, scale):
+    # scale 0.05 keeps every segment's difference inside the series branch
+    assert pins.dev_half_vs_quadrature(csa_half_reference, seed=seed, scale=scale) < 1e-12
+
+
+def test_half_interval_trapezoid_for_equal_logits():
+    assert pins.dev_half_trapezoid(csa_half_reference) < 1e-14
+
+
+@pytest.mark.parametrize("beta", [0.7, -1.3, 0.01])
+def test_half_interval_linear_ramp_closed_form(beta):
+    assert pins.dev_half_linear_ramp(csa_half_reference, beta=beta) < 1e-11
+
+
+def test_segment_integrals_reduce_to_phi_on_the_unit_segment():
+    x = np.concatenate([np.linspace(-6, 6, 49), [-0.51, -0.4999, 0.4999, 0.51, 0.0]])
+    f0, f1 = seg_integrals(x, 0.0, 1.0)
+    assert np.abs(f0 - phi1(x)).max() < 1e-13
+    assert np.abs((f0 - f1) - phi2(x)).max() < 1e-13
+    # additivity over [0, 1/2] + [1/2, 1]
+    a0, a1 = seg_integrals(x, 0.0, 0.5)
+    b0, b1 = seg_integrals(x, 0.5, 1.0)
+    assert np.abs(a0 + b0 - f0).max() < 1e-13 and np.abs(a1 + b1 - f1).max() < 1e-13

@@ -10,7 +10,8 @@ and standard attention "essentially the same" in FLOPs -- and the fraction of
 the MI355X dense bf16 MFMA peak.  The standard-attention kernel built on the
 same tiling (std_fwd) runs on the same inputs for the ratio, and so does the
 first-order variant (csa_forward_first_order, b as the second difference of the
-logits) -- the same kernel without the exact correction weights.  The ``decode``
+logits) -- the same kernel without the exact correction weights -- and the interval
+variant [1/2, t + 1/2] (csa_forward_half_interval), under the same FLOP count.  The ``decode``
 object times csa_decode (a few new queries against a key/value cache, bound by HBM
 bandwidth) on the decode workloads, and ``backward`` times csa_backward (the gradients
 dq, dk, dv, dk0, dv0 from the forward's o and lse and a seeded dO) on the same workload,
@@ -211,6 +212,9 @@ def counters_mode(w, q, k, v, k0, v0):
     if w.dtype == "bf16":
         csa.csa_forward_first_order(qd, kd, vd, k0d, v0d)
         torch.cuda.synchronize()
+        if w.d in (64, 128):
+            csa.csa_forward_half_interval(qd, kd, vd, k0d, v0d)
+            torch.cuda.synchronize()
         from workloads import make_grad_output
 
         o, lse = csa.csa_forward(qd, kd, vd, k0d, v0d)
@@ -238,6 +242,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-std", action="store_true")
     ap.add_argument("--no-first-order", action="store_true")
+    ap.add_argument("--no-half-interval", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-backward", action="store_true")
     ap.add_argument("--counters", action="store_true",
@@ -331,6 +336,17 @@ def main():
         res["first_order"] = {"value": round(f_tflops, 2), "unit": "TFLOP/s", "kernel_ms": round(f_avg, 4),
                               "pct_peak": round(100.0 * f_tflops / peak, 2),
                               "exact_over_first_order": round(tflops / f_tflops, 4)}
+    if not args.no_half_interval and w.dtype == "bf16" and w.d in (64, 128):
+        hout = torch.empty_like(qd)
+        hlse = torch.empty_like(lse)
+
+        def half_step():
+            csa.csa_forward_half_interval(qd, kd, vd, k0d, v0d, out=hout, lse=hlse, stream=stream)
+
+        h_avg, _, _ = time_kernel(half_step, args.steps, args.warmup, stream)
+        h_tflops = flop / (h_avg * 1e-3) / 1e12
+        res["half_interval"] = {"value": round(h_tflops, 2), "unit": "TFLOP/s", "kernel_ms": round(h_avg, 4),
+                                "pct_peak": round(100.0 * h_tflops / peak, 2)}
     if not args.no_backward and w.dtype == "bf16":
         from workloads import make_grad_output
 

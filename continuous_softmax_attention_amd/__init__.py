@@ -31,6 +31,9 @@ from ._lib import (  # noqa: F401
     csa_forward_first_order,
     csa_forward_first_order_check,
     csa_forward_first_order_raw,
+    csa_forward_half_interval,
+    csa_forward_half_interval_check,
+    csa_forward_half_interval_raw,
     csa_forward_raw,
     header_functions,
     library_path,

@@ -37,6 +37,8 @@ _SIGS = {
     "csa_forward_check": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, ctypes.c_int]),
     "csa_forward_first_order": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, ctypes.c_int, _vp]),
     "csa_forward_first_order_check": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, ctypes.c_int]),
+    "csa_forward_half_interval": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, ctypes.c_int, _vp]),
+    "csa_forward_half_interval_check": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, ctypes.c_int]),
     "csa_decode": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64, _i64,
                                   ctypes.c_int, _vp]),
     "csa_decode_check": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64, _i64,
@@ -103,6 +105,11 @@ def csa_forward_first_order_raw(q, k, v, k0, v0, out, lse, B, H, T, d, dtype, st
                                           stream or None)
 
 
+def csa_forward_half_interval_raw(q, k, v, k0, v0, out, lse, B, H, T, d, dtype, stream=0) -> int:
+    return load().csa_forward_half_interval(q, k, v, k0 or None, v0 or None, out, lse or None, B, H, T, d, dtype,
+                                            stream or None)
+
+
 def csa_decode_raw(q, k, v, k0, v0, out, lse, ws, ws_bytes, B, H, Tq, T, d, dtype, stream=0) -> int:
     return load().csa_decode(q, k, v, k0 or None, v0 or None, out, lse or None, ws, ws_bytes, B, H, Tq, T, d, dtype,
                              stream or None)
@@ -144,6 +151,10 @@ def csa_forward_check(q, k, v, k0, v0, out, lse, B, H, T, d, dtype) -> int:
 
 def csa_forward_first_order_check(q, k, v, k0, v0, out, lse, B, H, T, d, dtype) -> int:
     return load().csa_forward_first_order_check(q, k, v, k0, v0, out, lse, B, H, T, d, dtype)
+
+
+def csa_forward_half_interval_check(q, k, v, k0, v0, out, lse, B, H, T, d, dtype) -> int:
+    return load().csa_forward_half_interval_check(q, k, v, k0, v0, out, lse, B, H, T, d, dtype)
 
 
 def std_fwd_check(q, k, v, out, lse, B, H, T, d, dtype) -> int:
@@ -195,6 +206,12 @@ def csa_forward_first_order(q, k, v, k0=None, v0=None, *, out=None, lse=None, re
     """The first-order variant (b as the second difference of the logits, eq. (13)) through
     libcsa; bfloat16 only.  Same arguments and results as csa_forward."""
     return _csa_call("csa_forward_first_order", q, k, v, k0, v0, out, lse, return_lse, stream)
+
+
+def csa_forward_half_interval(q, k, v, k0=None, v0=None, *, out=None, lse=None, return_lse=True, stream=None):
+    """The interval variant [1/2, t + 1/2] (the original paper's choice, Problem Statement) through
+    libcsa; bfloat16, d in {64, 128}.  Same arguments and results as csa_forward."""
+    return _csa_call("csa_forward_half_interval", q, k, v, k0, v0, out, lse, return_lse, stream)
 
 
 def _csa_call(symbol, q, k, v, k0, v0, out, lse, return_lse, stream):

@@ -1,10 +1,11 @@
-// C-ABI entry points of libcsa: csa_forward, csa_forward_first_order, csa_decode and
-// csa_backward, each with its argument validation.
+// C-ABI entry points of libcsa: csa_forward, csa_forward_first_order,
+// csa_forward_half_interval, csa_decode and csa_backward, each with its argument validation.
 #include <hip/hip_runtime.h>
 
 #include "attn16.hpp"
 #include "bwd16.hpp"
 #include "decode.hpp"
+#include "half16.hpp"
 #include "attn_fwd.hpp"
 #include "csa.h"
 #include "validate.hpp"
@@ -41,6 +42,14 @@ int validate_first_order(const void* q, const void* k, const void* v, const void
   return dtype == CSA_BF16 ? CSA_OK : CSA_ERR_UNSUPPORTED;  // bf16 kernel only
 }
 
+int validate_half(const void* q, const void* k, const void* v, const void* k0, const void* v0,
+                  const void* out, const float* lse, int64_t B, int64_t H, int64_t T, int64_t d,
+                  int dtype) {
+  const int st = csa::validate(q, k, v, k0, v0, out, lse, B, H, T, d, dtype, true);
+  if (st != CSA_OK) return st;
+  return dtype == CSA_BF16 && (d == 64 || d == 128) ? CSA_OK : CSA_ERR_UNSUPPORTED;
+}
+
 }  // namespace
 
 extern "C" int csa_forward_check(const void* q, const void* k, const void* v, const void* k0,
@@ -73,6 +82,25 @@ extern "C" int csa_forward_first_order(const void* q, const void* k, const void*
   if (st != CSA_OK) return st;
   csa::FwdParams p{q, k, v, k0, v0, out, lse, (int)B, (int)H, (int)T, 0};
   return dispatch_first_order(p, d, (hipStream_t)stream);
+}
+
+extern "C" int csa_forward_half_interval_check(const void* q, const void* k, const void* v,
+                                               const void* k0, const void* v0, const void* out,
+                                               const float* lse, int64_t B, int64_t H, int64_t T,
+                                               int64_t d, int dtype) {
+  return validate_half(q, k, v, k0, v0, out, lse, B, H, T, d, dtype);
+}
+
+extern "C" int csa_forward_half_interval(const void* q, const void* k, const void* v,
+                                         const void* k0, const void* v0, void* out, float* lse,
+                                         int64_t B, int64_t H, int64_t T, int64_t d, int dtype,
+                                         void* stream) {
+  const int st = validate_half(q, k, v, k0, v0, out, lse, B, H, T, d, dtype);
+  if (st != CSA_OK) return st;
+  csa::FwdParams p{q, k, v, k0, v0, out, lse, (int)B, (int)H, (int)T, 0};
+  const hipError_t e = d == 64 ? csa::launch_half<64>(p, (hipStream_t)stream)
+                               : csa::launch_half<128>(p, (hipStream_t)stream);
+  return e == hipSuccess ? CSA_OK : CSA_ERR_HIP;
 }
 
 extern "C" const char* csa_status_string(int status) { return csa::status_string(status); }

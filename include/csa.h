@@ -1,7 +1,7 @@
 /*
  * libcsa -- causal continuous softmax attention on AMD Instinct MI355X (gfx950):
- * the forward pass, its first-order variant, few-query decoding against a cache, and the
- * backward pass.
+ * the forward pass, its first-order and half-interval variants, few-query decoding
+ * against a cache, and the backward pass.
  *
  * Method: J. Su, "Continuous Softmax Attention" (Scientific Spaces; English
  * translation on tylerromero.com).  Keys and values are linearly interpolated
@@ -110,6 +110,30 @@ int csa_forward_first_order(const void* q, const void* k, const void* v, const v
 int csa_forward_first_order_check(const void* q, const void* k, const void* v, const void* k0,
                                   const void* v0, const void* out, const float* lse, int64_t B,
                                   int64_t H, int64_t T, int64_t d, int dtype);
+
+/*
+ * csa_forward_half_interval -- the interval variant of "Continuous Softmax
+ * Attention" (Problem Statement: the original paper integrates eq. (2) over
+ * [1/2, t + 1/2] rather than [0, t]).  With the interpolation of eq. (3)
+ * unchanged, query t covers the upper half of segment [0, 1] (between k_0 and
+ * k_1), the whole segments [1, 2] .. [t-1, t], and the lower half of segment
+ * [t, t+1]: it reaches half a step toward position t+1.  For the last query
+ * (t = T) position T+1 is taken equal to position T, so that half segment is
+ * flat.  o_t is the ratio of the two integrals of eq. (2) over this interval and
+ * lse_t the natural log of the denominator integral.
+ *
+ * Arguments, layouts, ownership and return codes as csa_forward, except that
+ * dtype must be CSA_BF16 and d 64 or 128 (anything else returns
+ * CSA_ERR_UNSUPPORTED).
+ */
+int csa_forward_half_interval(const void* q, const void* k, const void* v, const void* k0,
+                              const void* v0, void* out, float* lse, int64_t B, int64_t H,
+                              int64_t T, int64_t d, int dtype, void* stream);
+
+/* The argument validation of csa_forward_half_interval alone (no HIP call). */
+int csa_forward_half_interval_check(const void* q, const void* k, const void* v, const void* k0,
+                                    const void* v0, const void* out, const float* lse, int64_t B,
+                                    int64_t H, int64_t T, int64_t d, int dtype);
 
 /*
  * csa_decode -- the forward for a few new queries against a key/value cache (decoding

@@ -41,9 +41,12 @@ _SERIES_RADIUS = 0.5
 _SERIES_TERMS = 20
 
 
-def seg_integrals(x, lo: float, hi: float):
-    """(F0, F1) = (integral_lo^hi e^{s x} ds, integral_lo^hi s e^{s x} ds), elementwise in x."""
+def seg_integrals(x, lo, hi):
+    """(F0, F1) = (integral_lo^hi e^{s x} ds, integral_lo^hi s e^{s x} ds), elementwise in x
+    (lo, hi: scalars or arrays broadcast against x)."""
     x = np.asarray(x, dtype=np.float64)
+    lo = np.asarray(lo, dtype=np.float64)
+    hi = np.asarray(hi, dtype=np.float64)
     small = np.abs(x) < _SERIES_RADIUS
     safe = np.where(small, 1.0, x)
     with np.errstate(over="ignore"):
@@ -71,16 +74,14 @@ def csa_half_row(q_t, k_hat, v_hat, t: int):
     V = v_hat[: t + 2]
     a = K @ q_t                         # positions 0..t+1
     shift = float(a.max())
-    num = np.zeros(V.shape[1])
-    den = 0.0
-    for i in range(1, t + 2):           # segment [i-1, i]
-        lo = 0.5 if i == 1 else 0.0
-        hi = 0.5 if i == t + 1 else 1.0
-        delta = a[i] - a[i - 1]
-        f0, f1 = (float(z) for z in seg_integrals(delta, lo, hi))
-        e = math.exp(a[i - 1] - shift)
-        num += e * ((f0 - f1) * V[i - 1] + f1 * V[i])
-        den += e * f0
+    i = np.arange(1, t + 2)             # segments [i-1, i], i = 1..t+1
+    lo = np.where(i == 1, 0.5, 0.0)     # covered part [lo, hi] of each segment's sigma
+    hi = np.where(i == t + 1, 0.5, 1.0)
+    delta = a[i] - a[i - 1]
+    f0, f1 = seg_integrals(delta, lo, hi)
+    e = np.exp(a[i - 1] - shift)
+    num = ((e * (f0 - f1))[:, None] * V[i - 1] + (e * f1)[:, None] * V[i]).sum(axis=0)
+    den = float((e * f0).sum())
     o = num / den
     lse = shift + math.log(den)
     if not (np.all(np.isfinite(o)) and math.isfinite(lse)):

@@ -35,6 +35,7 @@ def test_exports_every_declared_symbol(lib, header):
 
 def test_header_declares_the_entry_points():
     assert {"csa_forward", "csa_forward_check", "csa_forward_first_order", "csa_forward_first_order_check",
+            "csa_forward_half_interval", "csa_forward_half_interval_check",
             "csa_decode", "csa_decode_check", "csa_decode_workspace_bytes",
             "csa_backward", "csa_backward_check", "csa_backward_workspace_bytes",
             "csa_status_string"} <= set(csa.header_functions("csa.h"))
@@ -141,6 +142,31 @@ def test_first_order_check_rules():
     assert csa.csa_forward_first_order_raw(None, A, A, None, None, A + MB, None, 1, 1, 8, 64, csa.CSA_BF16) == INV
     assert csa.csa_forward_first_order_raw(A, A + MB, A + 2 * MB, None, None, A + 3 * MB, None, 1, 1, 8, 64,
                                            csa.CSA_F32) == UNS
+
+
+def _checkh(**kw):
+    a = _args(**kw)
+    return csa.csa_forward_half_interval_check(a["q"], a["k"], a["v"], a["k0"], a["v0"], a["out"], a["lse"],
+                                               a["B"], a["H"], a["T"], a["d"], a["dtype"])
+
+
+def test_half_interval_check_rules():
+    # same validation as csa_forward; bf16 and d in {64, 128} only
+    assert _checkh() == OK
+    assert _checkh(k0=A + 300 * MB, v0=A + 301 * MB, lse=None) == OK
+    for d in (64, 128):
+        assert _checkh(d=d) == OK
+        assert _checkh(d=d, dtype=csa.CSA_F32) == UNS
+    assert _checkh(d=16) == UNS
+    assert _checkh(d=96) == UNS
+    assert _checkh(q=None) == INV
+    assert _checkh(T=0) == INV
+    assert _checkh(out=A + 64 * MB + 4096) == INV
+    assert _checkh(v0=A + 301 * MB + 4) == INV
+    # the launching entry point rejects the same calls before any HIP call
+    assert csa.csa_forward_half_interval_raw(None, A, A, None, None, A + MB, None, 1, 1, 8, 64, csa.CSA_BF16) == INV
+    assert csa.csa_forward_half_interval_raw(A, A + MB, A + 2 * MB, None, None, A + 3 * MB, None, 1, 1, 8, 16,
+                                             csa.CSA_BF16) == UNS
 
 
 def _dargs(**kw):

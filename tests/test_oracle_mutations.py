@@ -149,12 +149,12 @@ def test_backward_mutant_is_caught(name):
 # ---------------------------------------------------------------- interval [1/2, t + 1/2]
 
 MUTATIONS_HALF = {
-    "left half taken as the whole segment": ("lo = 0.5 if i == 1 else 0.0", "lo = 0.0"),
-    "right half taken as the whole segment": ("hi = 0.5 if i == t + 1 else 1.0", "hi = 1.0"),
-    "right half segment dropped": ("for i in range(1, t + 2):", "for i in range(1, t + 1):"),
-    "halves swapped": ("lo = 0.5 if i == 1 else 0.0", "lo = 0.5 if i == t + 1 else 0.0"),
-    "weights of the two ends swapped": ("num += e * ((f0 - f1) * V[i - 1] + f1 * V[i])",
-                                        "num += e * (f1 * V[i - 1] + (f0 - f1) * V[i])"),
+    "left half taken as the whole segment": ("lo = np.where(i == 1, 0.5, 0.0)", "lo = np.zeros(i.shape)"),
+    "right half taken as the whole segment": ("hi = np.where(i == t + 1, 0.5, 1.0)", "hi = np.ones(i.shape)"),
+    "right half segment dropped": ("i = np.arange(1, t + 2)", "i = np.arange(1, t + 1)"),
+    "halves swapped": ("lo = np.where(i == 1, 0.5, 0.0)", "lo = np.where(i == t + 1, 0.5, 0.0)"),
+    "weights of the two ends swapped": ("(e * (f0 - f1))[:, None] * V[i - 1] + (e * f1)[:, None] * V[i]",
+                                        "(e * f1)[:, None] * V[i - 1] + (e * (f0 - f1))[:, None] * V[i]"),
     "series antiderivative power": ("(hi ** (n + 2) - lo ** (n + 2)) / (n + 2)", "(hi ** (n + 1) - lo ** (n + 1)) / (n + 2)"),
     "closed form of F1": ("(ehi * (hi * safe - 1.0) - elo * (lo * safe - 1.0))", "(ehi * (hi * safe + 1.0) - elo * (lo * safe + 1.0))"),
     "last query without the copied position": ("k[b, h, -1:]], axis=0)", "0 * k[b, h, -1:]], axis=0)"),

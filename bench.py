@@ -3,7 +3,9 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload lm] [--no-cpu-baseline]
 
 One step = one csa_forward call over the whole workload (every query row of
-every batch and head); inputs are resident in HBM before the timed region.
+every batch and head); inputs are resident in HBM before the timed region.  Each
+leg's untimed warm-up is W calls and at least --settle-s seconds of calls (default
+0.3 s): the GPU's clocks take ~50-100 ms of sustained load to ramp up.
 Metric: TFLOP/s counting 4 T^2 d / 2 FLOP per (batch, head) -- QK^T plus PV
 over the causal half, the convention under which the pages call continuous
 and standard attention "essentially the same" in FLOPs -- and the fraction of
@@ -132,13 +134,27 @@ def measured_traffic(workload_name):
 
 # ------------------------------------------------------------------ GPU leg
 
-def time_kernel(fn, steps, warmup, stream):
+SETTLE_S = 0.3  # untimed warm-up time per leg, at least (see time_kernel)
+
+
+def time_kernel(fn, steps, warmup, stream, settle_s=None):
     """Average per-launch duration (ms) from HIP events on the launch stream, and
-    the wall time (ms) of the whole timed region bracketed by synchronisations."""
+    the wall time (ms) of the whole timed region bracketed by synchronisations.
+
+    Warm-up: ``warmup`` untimed calls, continued (untimed) until at least ``settle_s``
+    seconds of them have run.  The GPU's clocks ramp up over the first ~50-100 ms of
+    sustained load (measured on the MI355X: 0.58 ms per lm call at the start, 0.46 ms
+    after ~100 calls); a handful of warm-up calls would time the ramp, not the kernel."""
     import torch
 
-    for _ in range(warmup):
+    settle_s = SETTLE_S if settle_s is None else settle_s
+    t_start = time.perf_counter()
+    n = 0
+    while n < warmup or (time.perf_counter() - t_start < settle_s and n < 20000):
         fn()
+        n += 1
+        if n % 50 == 0:
+            torch.cuda.synchronize()
     torch.cuda.synchronize()
     starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
     ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
@@ -234,11 +250,14 @@ def counters_mode(w, q, k, v, k0, v0):
 
 
 def main():
+    global SETTLE_S
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="lm")
+    ap.add_argument("--settle-s", type=float, default=SETTLE_S,
+                    help="untimed warm-up per leg lasts at least this long (GPU clock ramp)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-std", action="store_true")
     ap.add_argument("--no-first-order", action="store_true")
@@ -249,6 +268,7 @@ def main():
                     help="for rocprofv3 --pmc passes: one plain device copy of 256 MiB (counter "
                          "calibration), one csa_forward and one std_fwd launch, then exit")
     args = ap.parse_args()
+    SETTLE_S = args.settle_s
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: there is no multi-GPU path "
               "(independent (batch, head) shards need no communication); run with --gpus 1",

@@ -24,10 +24,14 @@ LIBS = {
 }
 
 # -packed-fp32-ops: no v_pk_{add,mul,fma}_f32 in the generated code.
+# -fno-honor-nans: no kernel produces or tests a NaN on purpose; without it every fmaxf
+# on a value the compiler cannot prove canonical (MFMA results, cross-lane moves) gets
+# an extra v_max_f32 x, x to quiet signalling NaNs.
 HIPCC_FLAGS = [
     "--offload-arch=gfx950",
     "-O3",
     "-std=c++17",
+    "-fno-honor-nans",
     "-fPIC",
     "-shared",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",

@@ -131,13 +131,20 @@ __global__ void __launch_bounds__(512, 2) half_fwd_kernel(FwdParams p) {
 #pragma unroll
     for (int s = 0; s < NSTEP; ++s) qreg[s] = *(const bf16x8*)(Qg + (4 * s + g) * 8);
   }
+  // query-wide reductions over the four lane groups (lanes n, n+16, n+32, n+48)
   auto qsum = [&](float x) {
-    x += __shfl_xor(x, 16);
-    return x + __shfl_xor(x, 32);
+    const unsigned u = __float_as_uint(x);
+    const auto r16 = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+    x = __uint_as_float(r16[0]) + __uint_as_float(r16[1]);
+    const Half h32 = pair_values(x);
+    return h32.lo + h32.hi;
   };
   auto qmax = [&](float x) {
-    x = fmaxf(x, __shfl_xor(x, 16));
-    return fmaxf(x, __shfl_xor(x, 32));
+    const unsigned u = __float_as_uint(x);
+    const auto r16 = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+    x = fmaxf(__uint_as_float(r16[0]), __uint_as_float(r16[1]));
+    const Half h32 = pair_values(x);
+    return fmaxf(h32.lo, h32.hi);
   };
   // logit of position 0 (zero when k0 is null)
   float a0 = 0.0f;
@@ -191,8 +198,9 @@ __global__ void __launch_bounds__(512, 2) half_fwd_kernel(FwdParams p) {
       if (g == 3 && (!masked || 16 <= vis)) mx = fmaxf(mx, sr);
       if (j == 0) mx = fmaxf(mx, a0);
       mx = qmax(mx);
+      // lazy shift: moves only when the maximum grows by more than 2^8 (weights stay <= 2^8)
       const float m_new = fmaxf(m_run, mx * kLog2e);
-      if (m_new > m_run) {
+      if (__builtin_amdgcn_ballot_w64(m_new > m_run + 8.0f) != 0) {
         const float sc = exp2_fast(m_run - m_new);
 #pragma unroll
         for (int mb = 0; mb < NMB; ++mb) O[mb] *= sc;
@@ -222,26 +230,43 @@ __global__ void __launch_bounds__(512, 2) half_fwd_kernel(FwdParams p) {
         }
         Lprev = L;
       }
+      // on masked tiles the edge (lim, lim+1) is this query's lower half segment: its
+      // endpoint values are kept while the loop passes and its terms added after it
+      float hA = 0.0f, hP = 0.0f, hB = 0.0f;
 #pragma unroll
       for (int t = 0; t < 16; ++t) {
         const float aN = alpha(t < 15 ? s[t + 1] : sr);
         const float pN = exp2_fast(aN);
         float R, L;
         edge_terms<false>(aC, pC, aN, pN, R, L);
-        if (masked) {  // edge (t, t+1): whole if t+1 <= lim, right half if t == lim, else absent
-          float HR, HL;
-          half::right_half(aC, pC, aN, HR, HL);
-          const float Rh = last_q ? 0.5f * half::kC2 * pC : HR;
-          const float Lh = last_q ? 0.0f : HL;
-          R = t + 1 <= lim ? R : (t == lim ? Rh : 0.0f);
-          L = t + 1 <= lim ? L : (t == lim ? Lh : 0.0f);
-          w[t] = t <= vis ? Lprev + R : 0.0f;
+        if (masked) {  // edge (t, t+1): whole if t+1 <= lim, else left out here
+          const bool whole = t + 1 <= lim;
+          hA = t == lim ? aC : hA;
+          hP = t == lim ? pC : hP;
+          hB = t == lim ? aN : hB;
+          w[t] = t <= vis ? Lprev + (whole ? R : 0.0f) : 0.0f;
+          L = whole ? L : 0.0f;
         } else {
           w[t] = Lprev + R;
         }
         Lprev = L;
         aC = aN;
         pC = pN;
+      }
+      if (masked) {
+        // lower half of segment (lim, lim+1): HR to key lim, HL to key lim+1; for the last
+        // query the segment is flat (position T+1 repeats T) and all of it, c^2 p/2, goes to
+        // key lim.  For lim = 15 the HL term belongs to the next lane group's key 0, which
+        // takes it from its own first edge.
+        float HR, HL;
+        half::right_half(hA, hP, hB, HR, HL);
+        const float Rh = last_q ? 0.5f * half::kC2 * hP : HR;
+        const float Lh = last_q ? 0.0f : HL;
+#pragma unroll
+        for (int t = 0; t < 16; ++t) {
+          w[t] = t == lim ? w[t] + Rh : w[t];
+          if (t > 0) w[t] = t == lim + 1 ? Lh : w[t];  // lim = -1: key 0 has its HL already
+        }
       }
       // O^T += V^T P^T and the row sums of the same rounded P
       const bf16x2 one2 = {(bf16)1.0f, (bf16)1.0f};

@@ -69,9 +69,15 @@ enum : int { kSoftmax = 0, kExact = 1, kFirstOrder = 2 };
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
 __device__ __forceinline__ void lds_copy16(const char* base, int voff, unsigned lds_addr) {
+  // base is wave-uniform by construction; the read-first-lane makes that explicit where the
+  // compiler's divergence analysis cannot see it (free when it can)
+  const uint64_t b = (uint64_t)(uintptr_t)base;
+  const unsigned lo = __builtin_amdgcn_readfirstlane((unsigned)b);
+  const unsigned hi = __builtin_amdgcn_readfirstlane((unsigned)(b >> 32));
+  const char* ub = (const char*)(uintptr_t)(((uint64_t)hi << 32) | lo);
   asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
                :
-               : "v"(voff), "s"(base), "s"(lds_addr)
+               : "v"(voff), "s"(ub), "s"(lds_addr)
                : "memory", "m0");
 }
 #pragma clang diagnostic pop

@@ -224,8 +224,18 @@ struct WaveTile {
   static constexpr int NSTEP = D / 32;
   static constexpr int NMB = D / 16;
   static constexpr int TILE = kTile * ROWB;  // 64 rows
-  static constexpr int HALO = 16 * ROWB;     // 16 rows: keys J-1, J+64, then 14 zero rows
+  // Halo block: 16 rows (keys J-1, J+64, then 14 zero rows) at a pitch of one row plus 16
+  // bytes, so that the 16 rows one lane group reads for an MFMA operand start on 16 different
+  // 16-byte bank slots (an unpadded pitch put all of them on the same banks).
+  static constexpr int HROW = ROWB + 16;
+  static constexpr int HALO = 16 * HROW;
 };
+
+// Byte offset of chunk `chunk` (0 .. 14 CH - 1) of the zero rows 2..15 of a halo block.
+template <int D>
+__device__ __forceinline__ int halo_zero_off(int chunk) {
+  return (2 + chunk / (D / 8)) * WaveTile<D>::HROW + 16 * (chunk % (D / 8));
+}
 
 // LDS read bases of a lane (the attn16 forms)
 __device__ __forceinline__ int row_kbase(int n, int g) { return (4 * (n & 3) + (n >> 2)) * 64 + 16 * (g ^ (n & 3)); }
@@ -274,15 +284,25 @@ __device__ __forceinline__ void neighbours(const float (&x)[16], const f32x4& H,
   right = g == 3 ? h1 : r;
 }
 
+// Source chunk and row (0 = left, 1 = right) of the 16-byte halo slot that lane `lane` fills
+// (lane i writes LDS bytes 16 i .. 16 i + 15 of the block): lanes 0 .. CH-1 fill row 0, lane CH
+// the pad after it (with a copy of row 1's chunk 0), lanes CH+1 .. 2 CH row 1.
+template <int D>
+__device__ __forceinline__ int halo_src_chunk(int lane, bool& right) {
+  constexpr int CH = D / 8;
+  right = lane >= CH;
+  return right ? max(lane - CH - 1, 0) : lane;
+}
+
 // Stage the halo rows: K rows (J-1, J+64) into halo rows 0, 1 and the same V rows into the
 // V halo, from per-lane addresses (row J-1 of position 0 is k0 / v0).  Wave-uniform caller.
 template <int D>
 __device__ __forceinline__ void stage_halo(CSA_LDS char* khalo, CSA_LDS char* vhalo, const char* kleft,
                                            const char* kright, const char* vleft, const char* vright, int lane) {
   constexpr int CH = D / 8;
-  if (lane < 2 * CH) {
-    const int c = lane % CH;
-    const bool right = lane >= CH;
+  if (lane <= 2 * CH) {
+    bool right;
+    const int c = halo_src_chunk<D>(lane, right);
     lds_copy16_ptr((right ? kright : kleft) + 16 * c,
                    __builtin_amdgcn_readfirstlane((unsigned)(uintptr_t)khalo));
     lds_copy16_ptr((right ? vright : vleft) + 16 * c,
@@ -373,7 +393,7 @@ __global__ void __launch_bounds__(512, 2) bwd_dq_kernel(BwdParams p) {
   for (int i = tid; i < 2 * 2 * 14 * CH; i += 512) {
     const int buf = i / (2 * 14 * CH), rest = i % (2 * 14 * CH);
     const int which = rest / (14 * CH), chunk = rest % (14 * CH);
-    *(CSA_LDS f32x4*)(lds + buf * BUF + 3 * TILE + which * HALO + 2 * ROWB + 16 * chunk) = f32x4{};
+    *(CSA_LDS f32x4*)(lds + buf * BUF + 3 * TILE + which * HALO + halo_zero_off<D>(chunk)) = f32x4{};
   }
 
   const int roff = row_layout_src<ROWB>(tid), toff = tr_layout_src<ROWB>(tid);
@@ -408,7 +428,7 @@ __global__ void __launch_bounds__(512, 2) bwd_dq_kernel(BwdParams p) {
   const int kbase = row_kbase(n, g);
   int vbase[2];
   tr_vbase(n, g, vbase);
-  const int hoff = n * ROWB + 16 * g;
+  const int hoff = n * WT::HROW + 16 * g;
 
   f32x4 acc[NMB];
 #pragma unroll
@@ -568,7 +588,7 @@ __global__ void __launch_bounds__(512, 2) bwd_dkdv_kernel(BwdParams p) {
 
   for (int i = tid; i < 2 * 14 * CH; i += 512) {
     const int which = i / (14 * CH), chunk = i % (14 * CH);
-    *(CSA_LDS f32x4*)(lds + OFF_KH + which * HALO + 2 * ROWB + 16 * chunk) = f32x4{};
+    *(CSA_LDS f32x4*)(lds + OFF_KH + which * HALO + halo_zero_off<D>(chunk)) = f32x4{};
   }
   const int roff = row_layout_src<ROWB>(tid), toff = tr_layout_src<ROWB>(tid);
   // the key block and its halo rows, once
@@ -583,7 +603,7 @@ __global__ void __launch_bounds__(512, 2) bwd_dkdv_kernel(BwdParams p) {
   const int kbase = row_kbase(n, g);
   int vbase[2];
   tr_vbase(n, g, vbase);
-  const int hoff = n * ROWB + 16 * g;
+  const int hoff = n * WT::HROW + 16 * g;
   // this wave's output blocks: 16 d-columns mb, 16-key blocks kc0 .. kc0 + KPW - 1
   const int mb = NMB == 8 ? wave : (wave & 3);
   const int kc0 = NMB == 8 ? 0 : 2 * (wave >> 2);

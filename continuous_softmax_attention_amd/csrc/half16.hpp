@@ -110,17 +110,19 @@ __global__ void __launch_bounds__(512, 2) half_fwd_kernel(FwdParams p) {
 
   for (int i = tid; i < 2 * 14 * CH; i += 512) {  // zero rows 2..15 of both halo buffers
     const int buf = i / (14 * CH), chunk = i % (14 * CH);
-    *(CSA_LDS f32x4*)(lds + buf * BUF + 2 * TILE + 2 * ROWB + 16 * chunk) = f32x4{};
+    *(CSA_LDS f32x4*)(lds + buf * BUF + 2 * TILE + halo_zero_off<D>(chunk)) = f32x4{};
   }
   const int roff = row_layout_src<ROWB>(tid), toff = tr_layout_src<ROWB>(tid);
   auto stage = [&](int buf, int tile) {
     CSA_LDS char* b = lds + buf * BUF;
     stage_tile<D>(b, Kg, tile * kTile, roff, Tn, wave);
     stage_tile<D>(b + TILE, Vg, tile * kTile, toff, Tn, wave);
-    if (wave == 0 && lane < 2 * CH) {  // halo rows J-1 (row 0 for the first tile) and J+64
+    if (wave == 0 && lane <= 2 * CH) {  // halo rows J-1 (row 0 for the first tile) and J+64
       const int J = tile * kTile;
-      const int row = lane < CH ? max(J - 1, 0) : min(J + kTile, Tn - 1);
-      lds_copy16_ptr(Kg + (size_t)row * ROWB + 16 * (lane % CH),
+      bool right;
+      const int c = halo_src_chunk<D>(lane, right);
+      const int row = right ? min(J + kTile, Tn - 1) : max(J - 1, 0);
+      lds_copy16_ptr(Kg + (size_t)row * ROWB + 16 * c,
                      __builtin_amdgcn_readfirstlane((unsigned)(uintptr_t)(b + 2 * TILE)));
     }
   };
@@ -163,7 +165,7 @@ __global__ void __launch_bounds__(512, 2) half_fwd_kernel(FwdParams p) {
   const int kbase = row_kbase(n, g);
   int vbase[2];
   tr_vbase(n, g, vbase);
-  const int hoff = n * ROWB + 16 * g;
+  const int hoff = n * WT::HROW + 16 * g;
   const bool last_q = qr == Tn - 1;
 
   f32x4 O[NMB];

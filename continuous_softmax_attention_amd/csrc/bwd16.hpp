@@ -147,7 +147,9 @@ __device__ __forceinline__ void lds_copy16_ptr(const char* src, unsigned lds_add
 // ---------------------------------------------------------------- per-element arithmetic
 // Edge (i, i+1) of one query from alpha_i, p_i, alpha_{i+1}, p_{i+1}: R/Z, L/Z and c_e as in
 // the header; all three zero when the edge does not exist (selects, so that values of
-// positions that do not exist for this query never reach the result).
+// positions that do not exist for this query never reach the result).  MASKED = false: the
+// caller knows that every edge exists and the selects are left out.
+template <bool MASKED>
 __device__ __forceinline__ void edge_grad(float al, float pl, float ar, float pr, bool exists, float& R,
                                           float& L, float& C) {
   constexpr float k0 = 0.2402265069591007f;     // c^2/2
@@ -169,15 +171,23 @@ __device__ __forceinline__ void edge_grad(float al, float pl, float ar, float pr
   r = ay < 0.07f ? rt : r;
   l = ay < 0.07f ? lt : l;
   c = ay < 0.25f ? ct : c;
-  R = exists ? r : 0.0f;
-  L = exists ? l : 0.0f;
-  C = exists ? c : 0.0f;
+  if constexpr (MASKED) {
+    R = exists ? r : 0.0f;
+    L = exists ? l : 0.0f;
+    C = exists ? c : 0.0f;
+  } else {
+    R = r;
+    L = l;
+    C = c;
+  }
 }
 
 // P and dS of one lane's 16 consecutive keys base+t of its query.  s/dp: logits and dO.v
 // of those keys; sl, dpl and sr, dpr: the same for keys base-1 and base+16.  Key base+t is
 // visible iff t <= lim.  Also returns P and dS of key base-1 as they follow from its right
-// edge alone: exact when key base-1 is position 0 (which has no left edge).
+// edge alone: exact when key base-1 is position 0 (which has no left edge).  MASKED = false
+// when every key of the tile and its right neighbour are visible (lim >= 16 in every lane).
+template <bool MASKED>
 __device__ __forceinline__ void tile_grad(const float (&s)[16], const float (&dp)[16], float sl, float dpl,
                                           float sr, float dpr, float mu, float delta, int lim, float (&P)[16],
                                           float (&dS)[16], float& p_left, float& ds_left) {
@@ -185,7 +195,7 @@ __device__ __forceinline__ void tile_grad(const float (&s)[16], const float (&dp
   float aC = alpha(sl), pC = exp2_fast(aC), dC = dpl;
   float aN = alpha(s[0]), pN = exp2_fast(aN), dN = dp[0];
   float R, L, C;
-  edge_grad(aC, pC, aN, pN, 0 <= lim, R, L, C);
+  edge_grad<MASKED>(aC, pC, aN, pN, 0 <= lim, R, L, C);
   float G = C * (dC - dN);
   p_left = R;
   ds_left = __builtin_fmaf(R, dC - delta, -G);
@@ -203,7 +213,7 @@ __device__ __forceinline__ void tile_grad(const float (&s)[16], const float (&dp
       dN = dpr;
     }
     pN = exp2_fast(aN);
-    edge_grad(aC, pC, aN, pN, t + 1 <= lim, R, L, C);
+    edge_grad<MASKED>(aC, pC, aN, pN, t + 1 <= lim, R, L, C);
     G = C * (dC - dN);
     const float pt = Lprev + R;
     P[t] = pt;
@@ -451,7 +461,10 @@ __global__ void __launch_bounds__(512, 2) bwd_dq_kernel(BwdParams p) {
       neighbours(dp, Hd, n, g, dl, dr);
       int lim = qr < Tn ? qr - (j * kTile + 16 * g) : -2;
       float P[16], dS[16], pl, dsl;
-      tile_grad(s, dp, sl, dl, sr, dr, mu, delta, lim, P, dS, pl, dsl);
+      // every edge of the tile exists for every query of the wave (rows past T only feed
+      // their own, unstored, dq rows)
+      if ((j + 1) * kTile <= qw) tile_grad<false>(s, dp, sl, dl, sr, dr, mu, delta, lim, P, dS, pl, dsl);
+      else tile_grad<true>(s, dp, sl, dl, sr, dr, mu, delta, lim, P, dS, pl, dsl);
       if (j == 0) {
         p0 = pl;
         ds0 = dsl;
@@ -649,7 +662,11 @@ __global__ void __launch_bounds__(512, 2) bwd_dkdv_kernel(BwdParams p) {
     neighbours(dp, Hd, n, g, dl, dr);
     const int lim = qr < Tn ? qr - (J + 16 * g) : -2;
     float P[16], dS[16], pl, dsl;
-    tile_grad(s, dp, sl, dl, sr, dr, mu, delta, lim, P, dS, pl, dsl);
+    // every edge exists for every query of the wave, and no row of the wave lies past T
+    // (those rows must contribute zeros to dK and dV)
+    const int qw = Q0 + 16 * wave;
+    if (qw >= J + kTile && qw + 15 < Tn) tile_grad<false>(s, dp, sl, dl, sr, dr, mu, delta, lim, P, dS, pl, dsl);
+    else tile_grad<true>(s, dp, sl, dl, sr, dr, mu, delta, lim, P, dS, pl, dsl);
     // keys 16g + 8h + e = chunks 2g + h of the P / dS row
 #pragma unroll
     for (int h = 0; h < 2; ++h) {

@@ -372,7 +372,8 @@ def main():
 
         dod = make_grad_output(q.shape, q.dtype, w.seed).to(dev)
         grads = [torch.empty_like(qd) for _ in range(3)]
-        bws = torch.empty(csa.csa_backward_workspace_bytes(w.B, w.H, w.T, w.d), dtype=torch.uint8, device=dev)
+        bws = torch.empty(csa.csa_backward_workspace_bytes_fast(w.B, w.H, w.T, w.d), dtype=torch.uint8,
+                          device=dev)
         csa.csa_forward(qd, kd, vd, k0d, v0d, out=out, lse=lse, stream=stream)
 
         def bwd_step():

@@ -47,6 +47,7 @@ _SIGS = {
     "csa_backward": (ctypes.c_int, [_vp] * 14 + [_i64] * 5 + [ctypes.c_int, _vp]),
     "csa_backward_check": (ctypes.c_int, [_vp] * 14 + [_i64] * 5 + [ctypes.c_int]),
     "csa_backward_workspace_bytes": (_i64, [_i64] * 4),
+    "csa_backward_workspace_bytes_fast": (_i64, [_i64] * 4),
     "csa_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "std_fwd": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, ctypes.c_int, _vp]),
     "std_fwd_check": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, ctypes.c_int]),
@@ -139,6 +140,12 @@ def csa_backward_check(q, k, v, k0, v0, o, lse, dout, dq, dk, dv, dk0, dv0, ws, 
 def csa_backward_workspace_bytes(B, H, T, d) -> int:
     """Bytes of workspace csa_backward needs (-1 for invalid sizes)."""
     return int(load().csa_backward_workspace_bytes(B, H, T, d))
+
+
+def csa_backward_workspace_bytes_fast(B, H, T, d) -> int:
+    """Bytes of workspace with which csa_backward keeps dS between its kernels (-1 for invalid
+    sizes); grows as T^2."""
+    return int(load().csa_backward_workspace_bytes_fast(B, H, T, d))
 
 
 def std_fwd_raw(q, k, v, out, lse, B, H, T, d, dtype, stream=0) -> int:
@@ -327,8 +334,9 @@ def csa_backward(q, k, v, o, lse, dout, k0=None, v0=None, *, sink_grads=True, dq
     q, k, v, o (the forward's output), dout: [B, H, T, d] bfloat16 device tensors; lse: the
     forward's [B, H, T] float32 lse; k0, v0: [B, H, d] or None (zeros).  Returns
     (dq, dk, dv, dk0, dv0) -- dk0 and dv0 ([B, H, d]) are None when sink_grads is False.
-    ``workspace``: a device tensor of at least csa_backward_workspace_bytes(B, H, T, d) bytes
-    (allocated here when None).
+    ``workspace``: a device tensor of at least csa_backward_workspace_bytes(B, H, T, d) bytes;
+    with csa_backward_workspace_bytes_fast(B, H, T, d) bytes or more dS is computed once
+    (allocated here when None, at the larger size).
     """
     import torch
 
@@ -348,7 +356,8 @@ def csa_backward(q, k, v, o, lse, dout, k0=None, v0=None, *, sink_grads=True, dq
     if need < 0:
         raise CsaError(CSA_ERR_UNSUPPORTED if d not in (64, 128) else CSA_ERR_INVALID_ARG, "csa_backward (sizes)")
     if workspace is None:
-        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+        workspace = torch.empty(max(need, csa_backward_workspace_bytes_fast(B, H, T, d)), dtype=torch.uint8,
+                                device=dev)
     grads = []
     for name, t in (("dq", dq), ("dk", dk), ("dv", dv)):
         if t is None:

@@ -65,7 +65,16 @@ struct BwdParams {
   void* dv0;  // may be null (not written)
   char* ws;   // workspace of csa_backward_workspace_bytes() bytes
   int B, H, T;
+  char* ds;          // dS tiles (optional last workspace region), or null: dq recomputes dS
+  int64_t ds_tiles;  // dS tiles per (b, h)
 };
+
+// dS tiles for the dq product: for every (b, h), query block qb (128 rows) and key tile
+// kb <= min(2 qb + 1, nkt - 1), 8 waves x 64 lanes x 16 bf16 -- each lane's 16 consecutive
+// keys of its query in the order of the dq product's B operand; qb (qb + 1) tiles precede
+// block qb.
+constexpr int kDsTileBytes = 8 * 64 * 32;
+__device__ __forceinline__ int64_t ds_tile_index(int qb, int kb) { return (int64_t)qb * (qb + 1) + kb; }
 
 // Workspace: 512 zero bytes (two rows of up to 128 bf16), then four float arrays of
 // B*H*T: D_t, mu_t, dS_{t,0}, P_{t,0}; then the float partial sums of dk_0 and dv_0,
@@ -507,6 +516,92 @@ __global__ void __launch_bounds__(512, 2) bwd_dq_kernel(BwdParams p) {
   }
 }
 
+// dq from the dS tiles bwd_dkdv<D, true> stored: the forward's decomposition (128 query rows
+// per work-group, wave w owns rows 16 w .. 16 w + 15), K tiles in the transposed LDS layout,
+// dQ^T += K^T dS^T on MFMAs with dS (bf16) read straight into the B operand; the same
+// products in the same order as bwd_dq, so the two paths give identical results.
+template <int D>
+__global__ void __launch_bounds__(512, 2) bwd_dq_from_ds_kernel(BwdParams p) {
+  using WT = WaveTile<D>;
+  constexpr int ROWB = WT::ROWB, NMB = WT::NMB, TILE = WT::TILE;
+  static_assert(D == 64 || D == 128, "head dimension");
+
+  __shared__ __attribute__((aligned(1024))) char smem[2 * TILE];  // K (transposed), two buffers
+  CSA_LDS char* lds = (CSA_LDS char*)smem;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int n = lane & 15, g = lane >> 4;
+  const int Tn = p.T, BH = p.B * p.H;
+  const int nqb = (Tn + kBlockRows - 1) / kBlockRows;
+  const int bh = blockIdx.x % BH;
+  const int qb = nqb - 1 - blockIdx.x / BH;  // longest query blocks first
+  const int q0 = qb * kBlockRows;
+  const int qw = q0 + 16 * wave;
+  const int qr = qw + n;
+  const bool wave_rows = qw < Tn;
+  const int jw = wave_rows ? min(qw + 15, Tn - 1) / kTile : -1;
+  const int jmax = min(q0 + kBlockRows - 1, Tn - 1) / kTile;
+  const BwdWs ws = bwd_ws(p.ws, BH, Tn);
+
+  const size_t head = (size_t)bh * (size_t)Tn * D;
+  const char* Kg = (const char*)((const bf16*)p.k + head);
+  const char* dsl = p.ds + ((size_t)bh * (size_t)p.ds_tiles + (size_t)ds_tile_index(qb, 0)) * kDsTileBytes +
+                    (size_t)(wave * 64 + lane) * 32;
+  const int toff = tr_layout_src<ROWB>(tid);
+  int vbase[2];
+  tr_vbase(n, g, vbase);
+
+  f32x4 acc[NMB];
+#pragma unroll
+  for (int mb = 0; mb < NMB; ++mb) acc[mb] = f32x4{};
+  bf16x8 bc[2], bn[2];
+  auto load_ds = [&](int j, bf16x8 (&b)[2]) {
+    const char* src = dsl + (size_t)j * kDsTileBytes;
+    b[0] = *(const bf16x8*)src;
+    b[1] = *(const bf16x8*)(src + 16);
+  };
+  if (jw >= 0) load_ds(0, bc);
+  stage_tile<D>(lds, Kg, 0, toff, Tn, wave);
+  wait_vmem();
+  __syncthreads();
+  for (int j = 0; j <= jmax; ++j) {
+    if (j + 1 <= jmax) stage_tile<D>(lds + ((j + 1) & 1) * TILE, Kg, (j + 1) * kTile, toff, Tn, wave);
+    if (j + 1 <= jw) load_ds(j + 1, bn);
+    if (j <= jw) {
+      CSA_LDS const char* b = lds + (j & 1) * TILE;
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+#pragma unroll
+        for (int mb = 0; mb < NMB; ++mb)
+          acc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(tr_read(b, vbase, c, mb), bc[c], acc[mb], 0, 0, 0);
+      }
+    }
+    bc[0] = bn[0];
+    bc[1] = bn[1];
+    wait_vmem();
+    __syncthreads();
+  }
+  if (!wave_rows || qr >= Tn) return;
+
+  // dq = (K^T dS^T)^T + dS_{t,0} k_0
+  const float ds0 = ws.ds0[(size_t)bh * Tn + qr];
+  const bf16* k0v = p.k0 ? (const bf16*)p.k0 + (size_t)bh * D : nullptr;
+  bf16* out = (bf16*)p.dq + head + (size_t)qr * D;
+#pragma unroll
+  for (int mb = 0; mb < NMB; ++mb) {
+    const int d0 = 16 * mb + 4 * g;
+    float o4[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      o4[r] = acc[mb][r];
+      if (k0v) o4[r] = __builtin_fmaf(ds0, (float)k0v[d0 + r], o4[r]);
+    }
+    *(bf16x4*)(out + d0) = bf16x4{(bf16)o4[0], (bf16)o4[1], (bf16)o4[2], (bf16)o4[3]};
+  }
+}
+
 // dk_0 = sum_t dS_{t,0} q_t and dv_0 = sum_t P_{t,0} dO_t in two passes: kSinkChunks
 // work-groups per (b, h) each sum a contiguous range of query rows into float32 partials
 // in the workspace; one work-group per (b, h) adds the partials (fixed order: the result
@@ -565,7 +660,9 @@ __global__ void __launch_bounds__(256) bwd_sink_final_kernel(BwdParams p) {
   }
 }
 
-template <int D>
+// WRITE_DS: also store this wave's dS into its dS tile (for bwd_dq_from_ds) and, for the
+// first key block, P and dS of position 0 (for the k_0 / v_0 gradients and dq's k_0 term).
+template <int D, bool WRITE_DS>
 __global__ void __launch_bounds__(512, 2) bwd_dkdv_kernel(BwdParams p) {
   using WT = WaveTile<D>;
   constexpr int CH = WT::CH, ROWB = WT::ROWB, NSTEP = WT::NSTEP, NMB = WT::NMB;
@@ -668,6 +765,15 @@ __global__ void __launch_bounds__(512, 2) bwd_dkdv_kernel(BwdParams p) {
     if (qw >= J + kTile && qw + 15 < Tn) tile_grad<false>(s, dp, sl, dl, sr, dr, mu, delta, lim, P, dS, pl, dsl);
     else tile_grad<true>(s, dp, sl, dl, sr, dr, mu, delta, lim, P, dS, pl, dsl);
     // keys 16g + 8h + e = chunks 2g + h of the P / dS row
+    char* dst = nullptr;
+    if constexpr (WRITE_DS) {
+      dst = p.ds + ((size_t)bh * (size_t)p.ds_tiles + (size_t)ds_tile_index(it, kb)) * kDsTileBytes +
+            (size_t)(wave * 64 + lane) * 32;
+      if (J == 0 && g == 0 && qr < Tn) {
+        ws.p0[(size_t)bh * Tn + qr] = pl;
+        ws.ds0[(size_t)bh * Tn + qr] = dsl;
+      }
+    }
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       bf16x8 pv, dv;
@@ -679,6 +785,7 @@ __global__ void __launch_bounds__(512, 2) bwd_dkdv_kernel(BwdParams p) {
       const int at = pt_off + tr_layout_at(prow, 2 * g + h);
       *(CSA_LDS bf16x8*)(lds + OFF_P + at) = pv;
       *(CSA_LDS bf16x8*)(lds + OFF_DS + at) = dv;
+      if constexpr (WRITE_DS) *(bf16x8*)(dst + 16 * h) = dv;
     }
     wait_vmem();
     __syncthreads();
@@ -722,13 +829,22 @@ inline hipError_t launch_backward(const BwdParams& prm, hipStream_t stream) {
   const int rpb = 4 * (64 / (D / 8));  // rows per pre block
   hipLaunchKernelGGL((bwd_pre_kernel<D>), dim3((unsigned)((rows + rpb - 1) / rpb)), dim3(256), 0, stream, prm);
   const int nqb = (prm.T + kBlockRows - 1) / kBlockRows;
-  hipLaunchKernelGGL((bwd_dq_kernel<D>), dim3((unsigned)(nqb * BH)), dim3(512), 0, stream, prm);
-  if (prm.dk0 != nullptr || prm.dv0 != nullptr) {
-    hipLaunchKernelGGL((bwd_sink_partial_kernel<D>), dim3((unsigned)(BH * kSinkChunks)), dim3(256), 0, stream, prm);
-    hipLaunchKernelGGL((bwd_sink_final_kernel<D>), dim3((unsigned)BH), dim3(256), 0, stream, prm);
-  }
   const int nkb = (prm.T + kTile - 1) / kTile;
-  hipLaunchKernelGGL((bwd_dkdv_kernel<D>), dim3((unsigned)(nkb * BH)), dim3(512), 0, stream, prm);
+  auto sink = [&]() {
+    if (prm.dk0 != nullptr || prm.dv0 != nullptr) {
+      hipLaunchKernelGGL((bwd_sink_partial_kernel<D>), dim3((unsigned)(BH * kSinkChunks)), dim3(256), 0, stream, prm);
+      hipLaunchKernelGGL((bwd_sink_final_kernel<D>), dim3((unsigned)BH), dim3(256), 0, stream, prm);
+    }
+  };
+  if (prm.ds != nullptr) {  // dS computed once (in bwd_dkdv) and stored; dq is then a plain product
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D, true>), dim3((unsigned)(nkb * BH)), dim3(512), 0, stream, prm);
+    sink();
+    hipLaunchKernelGGL((bwd_dq_from_ds_kernel<D>), dim3((unsigned)(nqb * BH)), dim3(512), 0, stream, prm);
+  } else {  // dS recomputed by bwd_dq (workspace without the dS tiles)
+    hipLaunchKernelGGL((bwd_dq_kernel<D>), dim3((unsigned)(nqb * BH)), dim3(512), 0, stream, prm);
+    sink();
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D, false>), dim3((unsigned)(nkb * BH)), dim3(512), 0, stream, prm);
+  }
   return hipGetLastError();
 }
 

@@ -108,6 +108,27 @@ inline int64_t backward_workspace_bytes(int64_t B, int64_t H, int64_t T, int64_t
   return 512 + 16 * B * H * T + B * H * 16 * 2 * 128 * 4;  // see bwd16.hpp for the layout
 }
 
+// Optional last region of the backward workspace: the bf16 dS tiles that let dq be a plain
+// product (bwd16.hpp).  Per (b, h): one 16 KiB tile per query block qb of 128 rows and key
+// tile kb <= min(2 qb + 1, nkt - 1) of 64 keys, i.e. qb (qb + 1) tiles before block qb.
+constexpr int64_t kBwdDsTileBytes = 8 * 64 * 32;  // 8 waves x 64 lanes x 16 bf16
+inline int64_t backward_ds_tiles_per_head(int64_t T) {
+  const int64_t nqb = (T + 127) / 128, nkt = (T + 63) / 64, last = nqb - 1;
+  const int64_t kmax = 2 * last + 1 < nkt - 1 ? 2 * last + 1 : nkt - 1;
+  return last * (last + 1) + kmax + 1;
+}
+inline int64_t backward_ds_offset(int64_t B, int64_t H, int64_t T, int64_t d) {
+  const int64_t base = backward_workspace_bytes(B, H, T, d);
+  return base < 0 ? -1 : (base + 255) / 256 * 256;
+}
+inline int64_t backward_workspace_bytes_fast(int64_t B, int64_t H, int64_t T, int64_t d) {
+  const int64_t off = backward_ds_offset(B, H, T, d);
+  if (off < 0) return -1;
+  const int64_t tiles = backward_ds_tiles_per_head(T);
+  if (tiles > (int64_t(1) << 62) / kBwdDsTileBytes / (B * H)) return -1;
+  return off + B * H * tiles * kBwdDsTileBytes;
+}
+
 inline int validate_backward(const void* q, const void* k, const void* v, const void* k0, const void* v0,
                              const void* o, const float* lse, const void* dout, const void* dq, const void* dk,
                              const void* dv, const void* dk0, const void* dv0, const void* ws, int64_t ws_bytes,
@@ -115,8 +136,10 @@ inline int validate_backward(const void* q, const void* k, const void* v, const 
   if (dtype != CSA_BF16) return CSA_ERR_UNSUPPORTED;
   if (d != 64 && d != 128) return CSA_ERR_UNSUPPORTED;
   if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv || !ws) return CSA_ERR_INVALID_ARG;
-  const int64_t need = backward_workspace_bytes(B, H, T, d);
-  if (need < 0 || ws_bytes < need) return CSA_ERR_INVALID_ARG;
+  const int64_t need_min = backward_workspace_bytes(B, H, T, d);
+  if (need_min < 0 || ws_bytes < need_min) return CSA_ERR_INVALID_ARG;
+  const int64_t need_fast = backward_workspace_bytes_fast(B, H, T, d);
+  const int64_t need = need_fast > 0 && ws_bytes >= need_fast ? need_fast : need_min;  // the part used
   for (const void* p : {q, k, v, o, dout, dq, dk, dv, ws})
     if (!aligned(p, 16)) return CSA_ERR_INVALID_ARG;
   for (const void* p : {k0, v0, dk0, dv0})

@@ -191,7 +191,9 @@ int64_t csa_decode_workspace_bytes(int64_t B, int64_t H, int64_t Tq, int64_t T, 
  *              when k0 / v0 is NULL (the gradient at the zero vector).
  *   workspace  device, 16-byte aligned, at least csa_backward_workspace_bytes(B, H, T, d)
  *              bytes, caller-owned scratch (no initialisation needed); calls sharing it must be
- *              ordered on one stream.
+ *              ordered on one stream.  With at least csa_backward_workspace_bytes_fast(B, H, T,
+ *              d) bytes the call also keeps dS (bf16, about B*H*T*T bytes) so that it is
+ *              computed once instead of twice; the results are identical either way.
  *   d          64 or 128 (16 returns CSA_ERR_UNSUPPORTED); dtype must be CSA_BF16.
  *   stream     hipStream_t or NULL.
  *
@@ -215,6 +217,13 @@ int csa_backward_check(const void* q, const void* k, const void* v, const void* 
 
 /* Workspace bytes csa_backward needs for these sizes, or -1 if the sizes are invalid. */
 int64_t csa_backward_workspace_bytes(int64_t B, int64_t H, int64_t T, int64_t d);
+
+/*
+ * Workspace bytes with which csa_backward keeps dS between its kernels (the faster path;
+ * grows as T^2: about B*H*T*T bytes), or -1 if the sizes are invalid or that size does not
+ * fit in an int64.
+ */
+int64_t csa_backward_workspace_bytes_fast(int64_t B, int64_t H, int64_t T, int64_t d);
 
 /* Static, NUL-terminated description of a return code. */
 const char* csa_status_string(int status);

@@ -244,6 +244,30 @@ def test_backward_workspace_size():
         assert csa.csa_backward_workspace_bytes(a["B"], a["H"], a["T"], a["d"]) == -1
 
 
+def _ds_tiles_brute(T):
+    # (query block of 128 rows, key tile of 64 keys) pairs with the key tile at or before the
+    # tile holding the block's last row
+    nqb = (T + 127) // 128
+    return sum(min(qb * 128 + 127, T - 1) // 64 + 1 for qb in range(nqb))
+
+
+@pytest.mark.parametrize("T", [1, 2, 63, 64, 65, 127, 128, 129, 191, 192, 193, 255, 256, 257, 1000, 4096, 16384])
+def test_backward_fast_workspace_size(T):
+    base = csa.csa_backward_workspace_bytes(2, 3, T, 128)
+    fast = csa.csa_backward_workspace_bytes_fast(2, 3, T, 128)
+    off = (base + 255) // 256 * 256
+    assert fast == off + 2 * 3 * _ds_tiles_brute(T) * 8 * 64 * 32
+    assert csa.csa_backward_workspace_bytes_fast(1, 1, T, 16) == -1
+
+
+def test_backward_check_accepts_either_workspace():
+    a = _bargs()
+    lo = csa.csa_backward_workspace_bytes(a["B"], a["H"], a["T"], a["d"])
+    hi = csa.csa_backward_workspace_bytes_fast(a["B"], a["H"], a["T"], a["d"])
+    assert hi > lo
+    assert _bcheck(wsb=lo) == OK and _bcheck(wsb=hi) == OK and _bcheck(wsb=lo - 16) == INV
+
+
 def test_backward_check_rules():
     assert _bcheck() == OK
     assert _bcheck(d=128) == OK

@@ -134,6 +134,25 @@ def test_workspace_reuse_with_smaller_second_call():
         _compare(f"workspace reuse T{T}", got, csa_backward_reference(q, k, v, do, k0, v0))
 
 
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("T", [1, 2, 63, 64, 65, 127, 128, 129, 200, 300, 1000])
+def test_kept_ds_and_recomputed_ds_paths_agree_bitwise(T, d):
+    # with csa_backward_workspace_bytes_fast bytes dS is computed once (bwd_dkdv) and kept
+    # for dq; with the minimum it is recomputed (bwd_dq).  Same products, same order: the
+    # results must be identical, bit for bit (the fast path is also checked against the
+    # reference by every other test here, which use the binding's default workspace).
+    q, k, v, k0, v0, do = _random_case(2, 2, T, d, seed=3000 + T + d)
+    qg, kg, vg, k0g, v0g, dog = _gpu(q, k, v, k0, v0, do)
+    o, lse = csa.csa_forward(qg, kg, vg, k0g, v0g)
+    lo = torch.empty(csa.csa_backward_workspace_bytes(2, 2, T, d), dtype=torch.uint8, device=DEV)
+    hi = torch.empty(csa.csa_backward_workspace_bytes_fast(2, 2, T, d), dtype=torch.uint8, device=DEV)
+    a = [_np(g) for g in csa.csa_backward(qg, kg, vg, o, lse, dog, k0g, v0g, workspace=lo)]
+    b = [_np(g) for g in csa.csa_backward(qg, kg, vg, o, lse, dog, k0g, v0g, workspace=hi)]
+    torch.cuda.synchronize()
+    for name, x, y in zip(NAMES, a, b):
+        assert np.array_equal(x, y), name
+
+
 def test_rejects_unsupported_before_launch():
     q = torch.zeros(1, 1, 8, 64, device=DEV)
     lse = torch.zeros(1, 1, 8, device=DEV)

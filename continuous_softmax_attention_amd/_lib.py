@@ -336,7 +336,8 @@ def csa_backward(q, k, v, o, lse, dout, k0=None, v0=None, *, sink_grads=True, dq
     (dq, dk, dv, dk0, dv0) -- dk0 and dv0 ([B, H, d]) are None when sink_grads is False.
     ``workspace``: a device tensor of at least csa_backward_workspace_bytes(B, H, T, d) bytes;
     with csa_backward_workspace_bytes_fast(B, H, T, d) bytes or more dS is computed once
-    (allocated here when None, at the larger size).
+    (allocated here when None: the larger size while it is at most a quarter of the free device
+    memory, else the smaller).
     """
     import torch
 
@@ -356,8 +357,12 @@ def csa_backward(q, k, v, o, lse, dout, k0=None, v0=None, *, sink_grads=True, dq
     if need < 0:
         raise CsaError(CSA_ERR_UNSUPPORTED if d not in (64, 128) else CSA_ERR_INVALID_ARG, "csa_backward (sizes)")
     if workspace is None:
-        workspace = torch.empty(max(need, csa_backward_workspace_bytes_fast(B, H, T, d)), dtype=torch.uint8,
-                                device=dev)
+        # the kept-dS workspace grows as T^2: take it only while it is a modest share of the
+        # free device memory, else the O(B H T) workspace (dS recomputed; identical results)
+        fast = csa_backward_workspace_bytes_fast(B, H, T, d)
+        free, _ = torch.cuda.mem_get_info(dev)
+        size = fast if 0 < fast <= free // 4 else need
+        workspace = torch.empty(size, dtype=torch.uint8, device=dev)
     grads = []
     for name, t in (("dq", dq), ("dk", dk), ("dv", dv)):
         if t is None:

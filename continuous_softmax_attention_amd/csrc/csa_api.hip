@@ -123,7 +123,7 @@ extern "C" int csa_decode(const void* q, const void* k, const void* v, const voi
       csa::validate_decode(q, k, v, k0, v0, out, lse, workspace, workspace_bytes, B, H, Tq, T, d, dtype);
   if (st != CSA_OK) return st;
   csa::DecParams p{q, k, v, k0, v0, out, lse, (float*)workspace,
-                   (int)(B * H), (int)Tq, (int)T, csa::decode_splits(T)};
+                   (int)(B * H), (int)Tq, (int)T, 0, 0};  // split plan chosen at launch
   hipStream_t s = (hipStream_t)stream;
   hipError_t e = hipErrorInvalidValue;
   if (dtype == CSA_F32) {

@@ -10,9 +10,11 @@
 // key and query, so it is bound by HBM bandwidth, not by the matrix cores: it is
 // written for streaming, not for MFMA.
 //
-//   Pass 1 (decode_partial_kernel): one wave per (batch*head, split) where a split is
-//   256 consecutive positions (the kernel is instantiated for at most 1, 2, 4 or 8
-//   queries, so that small Tq keep few registers and many waves in flight).  Blocks of 64 positions, one position per lane:
+//   Pass 1 (decode_partial_kernel): one wave per (batch*head, split) where a split is a run
+//   of 64 .. 1024 consecutive positions, its length chosen per call so that the waves fill
+//   the device in whole rounds (decode_chunk; the kernel is instantiated for at most 1, 2, 4
+//   or 8 queries, so that small Tq keep few registers and many waves in flight).  Blocks of
+//   64 positions, one position per lane:
 //     * logits q_j . k_p for the Tq queries (lane = position; q broadcast from LDS;
 //       v_dot2_f32_bf16 for bf16);
 //     * neighbours through ds_bpermute inside the block; across blocks from the
@@ -38,7 +40,6 @@
 
 namespace csa {
 
-constexpr int kDecChunk = 256;  // positions per split
 constexpr int kDecMaxQ = 8;     // queries per call
 constexpr int kDecWaves = 4;    // splits per work-group (one per wave)
 
@@ -52,11 +53,29 @@ struct DecParams {
   float* lse;      // [B, H, Tq] or null
   float* ws;       // [B*H, nsplit, Tq, d + 2] float32
   int BH, Tq, T, nsplit;
+  int chunk;       // positions per split (a multiple of 64)
 };
 
-inline int decode_splits(int64_t T) { return (int)((T + 1 + kDecChunk - 1) / kDecChunk); }
-inline int64_t decode_workspace_floats(int64_t BH, int64_t Tq, int64_t T, int64_t d) {
-  return BH * decode_splits(T) * Tq * (d + 2);
+// Positions per split for B*H heads of T cached positions when `cap` waves of the partial
+// kernel fit on the device at once: every split is one wave, and a wave's time grows with its
+// number of 64-position blocks, so the call takes about rounds x (blocks per split + a fixed
+// cost) -- choose the split length (1 .. 16 blocks) that minimises it.  A fixed length of 256
+// positions put, e.g., 128 heads x 8193 positions into 33 splits per head: 4224 waves for 4096
+// slots, a second round for the last 3% and half the bandwidth.
+inline int decode_chunk(int64_t BH, int64_t T, int64_t cap) {
+  const int64_t blocks = (T + 1 + 63) / 64;
+  int best = 4;
+  double best_t = 1e300;
+  for (int cb = 1; cb <= 16; ++cb) {
+    const int64_t ns = (blocks + cb - 1) / cb;
+    const int64_t rounds = (BH * ns + cap - 1) / cap;
+    const double t = (double)rounds * (cb + 0.5);
+    if (t <= best_t) {  // ties: the longer splits (fewer partial results to merge)
+      best_t = t;
+      best = cb;
+    }
+  }
+  return 64 * best;
 }
 
 __device__ __forceinline__ float wave_max(float x) {
@@ -120,8 +139,8 @@ __global__ void __launch_bounds__(64 * kDecWaves) decode_partial_kernel(DecParam
   const int sp = item % p.nsplit;
   const int Tn = p.T;
   const int Tq = p.Tq;
-  const int p0 = sp * kDecChunk;
-  const int pend = min(p0 + kDecChunk, Tn + 1);  // this split owns positions [p0, pend)
+  const int p0 = sp * p.chunk;
+  const int pend = min(p0 + p.chunk, Tn + 1);  // this split owns positions [p0, pend)
   const int nb = (pend - p0 + 63) / 64;
 
   // queries of this head into the wave's LDS slice (read back as broadcasts)
@@ -368,15 +387,42 @@ __global__ void __launch_bounds__(64) decode_merge_kernel(DecParams p) {
     p.lse[(size_t)bh * p.Tq + j] = (M + __builtin_amdgcn_logf(L)) * kLn2 + 0.7330258411633287f;  // -2 ln(ln 2)
 }
 
+// Work-groups of the partial kernel resident per CU (the same on every gfx950 device: a
+// property of the compiled kernel), queried once.
+template <typename TT, int D, int QMAX>
+inline int decode_blocks_per_cu() {
+  static const int n = [] {
+    int b = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&b, decode_partial_kernel<TT, D, QMAX>, 64 * kDecWaves, 0) !=
+        hipSuccess)
+      b = 0;
+    return b;
+  }();
+  return n;
+}
+
+// prm.BH, Tq, T set; fills in chunk and nsplit for this device and launches both passes.
 template <typename TT, int D>
-inline hipError_t launch_decode(const DecParams& prm, hipStream_t stream) {
+inline hipError_t launch_decode(const DecParams& prm_in, hipStream_t stream) {
+  DecParams prm = prm_in;
+  int dev = 0, cus = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return e;
+  const int bpc = prm.Tq <= 1   ? decode_blocks_per_cu<TT, D, 1>()
+                  : prm.Tq <= 2 ? decode_blocks_per_cu<TT, D, 2>()
+                  : prm.Tq <= 4 ? decode_blocks_per_cu<TT, D, 4>()
+                                : decode_blocks_per_cu<TT, D, 8>();
+  const int64_t cap = (int64_t)(bpc > 0 ? bpc : 1) * kDecWaves * (cus > 0 ? cus : 1);
+  prm.chunk = decode_chunk(prm.BH, prm.T, cap);
+  prm.nsplit = (prm.T + 1 + prm.chunk - 1) / prm.chunk;
   const int items = prm.BH * prm.nsplit;
   const dim3 grid((items + kDecWaves - 1) / kDecWaves), block(64 * kDecWaves);
   if (prm.Tq <= 1) hipLaunchKernelGGL((decode_partial_kernel<TT, D, 1>), grid, block, 0, stream, prm);
   else if (prm.Tq <= 2) hipLaunchKernelGGL((decode_partial_kernel<TT, D, 2>), grid, block, 0, stream, prm);
   else if (prm.Tq <= 4) hipLaunchKernelGGL((decode_partial_kernel<TT, D, 4>), grid, block, 0, stream, prm);
   else hipLaunchKernelGGL((decode_partial_kernel<TT, D, 8>), grid, block, 0, stream, prm);
-  hipError_t e = hipGetLastError();
+  e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((decode_merge_kernel<TT, D>), dim3(prm.BH * prm.Tq), dim3(64), 0, stream, prm);
   return hipGetLastError();

@@ -67,7 +67,7 @@ inline int64_t decode_workspace_bytes(int64_t B, int64_t H, int64_t Tq, int64_t 
   if (d != 16 && d != 64 && d != 128) return -1;
   const int64_t kMax32 = (int64_t(1) << 31) - 1;
   if (T > kMax32 / 2 || B > kMax32 || H > kMax32 || B * H > kMax32) return -1;
-  const int64_t nsplit = (T + 1 + 255) / 256;  // splits of 256 positions
+  const int64_t nsplit = (T + 1 + 63) / 64;  // at most one split per 64 positions
   if (B * H > kMax32 / nsplit) return -1;
   return B * H * nsplit * Tq * (d + 2) * 4;
 }

@@ -185,10 +185,11 @@ def _dcheck(**kw):
 
 
 def test_decode_workspace_size():
-    # one (O[d], m, l) float32 record per (head, split of 256 positions, query)
-    assert csa.csa_decode_workspace_bytes(2, 3, 4, 1000, 128) == 2 * 3 * 4 * 4 * 130 * 4
-    assert csa.csa_decode_workspace_bytes(1, 1, 1, 255, 64) == 1 * 1 * 1 * 1 * 66 * 4
-    assert csa.csa_decode_workspace_bytes(1, 1, 1, 256, 64) == 2 * 66 * 4
+    # one (O[d], m, l) float32 record per (head, split, query), with room for one split per
+    # 64 of the T + 1 positions (the call picks the split length)
+    assert csa.csa_decode_workspace_bytes(2, 3, 4, 1000, 128) == 2 * 3 * 16 * 4 * 130 * 4
+    assert csa.csa_decode_workspace_bytes(1, 1, 1, 255, 64) == 4 * 66 * 4
+    assert csa.csa_decode_workspace_bytes(1, 1, 1, 256, 64) == 5 * 66 * 4
     for bad in (dict(Tq=0), dict(Tq=9), dict(Tq=5, T=4), dict(d=32), dict(B=0), dict(T=0)):
         a = dict(B=1, H=1, Tq=1, T=100, d=64)
         a.update(bad)

@@ -31,6 +31,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
+#include <type_traits>
 
 #include "bwd16.hpp"
 
@@ -177,7 +178,9 @@ __global__ void __launch_bounds__(512, 2) half_fwd_kernel(FwdParams p) {
   stage(0, 0);
   wait_vmem();
   __syncthreads();
-  for (int j = 0; j <= jmax; ++j) {
+  // one key tile: MASKED when some key or edge of it is cut for some query of the wave
+  auto iter = [&](int j, auto masked_c) {
+    constexpr bool masked = decltype(masked_c)::value;
     if (j + 1 <= jmax) stage((j + 1) & 1, j + 1);
     if (j <= jw) {
       CSA_LDS const char* b = lds + (j & 1) * BUF;
@@ -191,7 +194,6 @@ __global__ void __launch_bounds__(512, 2) half_fwd_kernel(FwdParams p) {
       if (start) sl = a0;
       const int lim = qr < Tn ? qr - (J + 16 * g) : -3;   // key t is position <= t_query iff t <= lim
       const int vis = last_q ? lim : lim + 1;              // last visible key of this lane
-      const bool masked = J + kTile > qw;                  // some key or edge of the tile is cut
 
       // running maximum over visible keys, the right halo when visible, and position 0
       float mx = -__builtin_inff();
@@ -225,7 +227,7 @@ __global__ void __launch_bounds__(512, 2) half_fwd_kernel(FwdParams p) {
           half::left_half(aP, pP, aC, pC, HRl, HLl);
           if (j == 0) w0 = HRl;
           L = HLl;
-        } else if (masked) {
+        } else if constexpr (masked) {
           float HR, HL;
           half::right_half(aP, pP, aC, HR, HL);
           L = lim >= 0 ? L : (lim == -1 && !last_q ? HL : 0.0f);
@@ -241,7 +243,7 @@ __global__ void __launch_bounds__(512, 2) half_fwd_kernel(FwdParams p) {
         const float pN = exp2_fast(aN);
         float R, L;
         edge_terms<false>(aC, pC, aN, pN, R, L);
-        if (masked) {  // edge (t, t+1): whole if t+1 <= lim, else left out here
+        if constexpr (masked) {  // edge (t, t+1): whole if t+1 <= lim, else left out here
           const bool whole = t + 1 <= lim;
           hA = t == lim ? aC : hA;
           hP = t == lim ? pC : hP;
@@ -255,7 +257,7 @@ __global__ void __launch_bounds__(512, 2) half_fwd_kernel(FwdParams p) {
         aC = aN;
         pC = pN;
       }
-      if (masked) {
+      if constexpr (masked) {
         // lower half of segment (lim, lim+1): HR to key lim, HL to key lim+1; for the last
         // query the segment is flat (position T+1 repeats T) and all of it, c^2 p/2, goes to
         // key lim.  For lim = 15 the HL term belongs to the next lane group's key 0, which
@@ -287,7 +289,12 @@ __global__ void __launch_bounds__(512, 2) half_fwd_kernel(FwdParams p) {
     }
     wait_vmem();
     __syncthreads();
-  }
+  };
+  // tiles entirely below the wave's diagonal (no masks), then the others
+  const int jm = wave_rows ? qw / kTile : 0;
+  int j = 0;
+  for (; j < jm; ++j) iter(j, std::false_type{});
+  for (; j <= jmax; ++j) iter(j, std::true_type{});
   if (!wave_rows) return;
 
   float l = qsum(lsum);

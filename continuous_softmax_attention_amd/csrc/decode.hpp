@@ -36,7 +36,7 @@
 
 #include <cstdint>
 
-#include "attn_fwd.hpp"
+#include "attn16.hpp"
 
 namespace csa {
 
@@ -128,7 +128,14 @@ __global__ void __launch_bounds__(64 * kDecWaves) decode_partial_kernel(DecParam
   typedef float f32x4v __attribute__((ext_vector_type(4)));
   typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
 
+  constexpr int ROWB = NCH * 16;             // bytes per row
+  constexpr int NST = 32 * ROWB / 1024;      // 1 KiB copy instructions per 32-row stage
+  static_assert(NST >= 1 && 32 * ROWB % 1024 == 0, "stage size");
   __shared__ __attribute__((aligned(16))) TT qs[kDecWaves][QMAX][D];
+  // K rows of 32 positions at a time, per wave: row r at r * ROWB, its 16-byte chunk cc at
+  // position cc ^ (r & (NCH - 1)) -- filled by whole-KiB (coalesced) global_load_lds copies,
+  // read back one row per lane without bank conflicts
+  __shared__ __attribute__((aligned(1024))) char kst[kDecWaves][32 * ROWB];
   static_assert(QMAX >= 1 && QMAX <= kDecMaxQ, "query bound");
 
   const int lane = threadIdx.x & 63;
@@ -157,40 +164,6 @@ __global__ void __launch_bounds__(64 * kDecWaves) decode_partial_kernel(DecParam
   auto krow = [&](int pos) -> const TT* { return pos == 0 ? K0 : Kh + (size_t)(pos - 1) * D; };
   auto vrow = [&](int pos) -> const TT* { return pos == 0 ? V0 : Vh + (size_t)(pos - 1) * D; };
 
-  // logits of position pos (per lane) for every query; 0 where the row does not exist
-  auto logits = [&](int pos, float (&a)[QMAX]) {
-#pragma unroll
-    for (int j = 0; j < QMAX; ++j) a[j] = 0.0f;
-    const TT* row = pos <= Tn ? krow(pos) : nullptr;
-    if (row == nullptr) return;
-    f32x4v kc[NCH];
-#pragma unroll
-    for (int c = 0; c < NCH; ++c) kc[c] = *(const f32x4v*)(row + c * EPC);  // 16 bytes
-#pragma unroll
-    for (int j = 0; j < QMAX; ++j) {
-      if (j < Tq) {
-        float acc = 0.0f;
-#pragma unroll
-        for (int c = 0; c < NCH; ++c) {
-          const f32x4v qc = *(const f32x4v*)&qs[wv][j][c * EPC];  // broadcast read
-          if constexpr (F32) {
-#pragma unroll
-            for (int e = 0; e < 4; ++e) acc = __builtin_fmaf(kc[c][e], qc[e], acc);
-          } else {
-            // whole-chunk bit casts, then element pairs (a bit cast of a single vector
-            // element would read element 0)
-            const bf16x8 kb = __builtin_bit_cast(bf16x8, kc[c]);
-            const bf16x8 qb = __builtin_bit_cast(bf16x8, qc);
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-              acc = __builtin_amdgcn_fdot2_f32_bf16(bf16x2v{kb[2 * e], kb[2 * e + 1]},
-                                                    bf16x2v{qb[2 * e], qb[2 * e + 1]}, acc, false);
-          }
-        }
-        a[j] = acc;
-      }
-    }
-  };
   // logits of one (wave-uniform) position, lane-parallel over d; 0 if it does not exist
   auto halo = [&](int pos, float (&a)[QMAX]) {
 #pragma unroll
@@ -214,6 +187,78 @@ __global__ void __launch_bounds__(64 * kDecWaves) decode_partial_kernel(DecParam
     }
   };
 
+  // logits of positions base + lane for every query; 0 where the row does not exist.  Two
+  // stages of 32 rows: each row's K is staged in LDS by coalesced copies, lanes r and r + 32
+  // each take half of row r (lane-per-row loads straight from HBM reached ~4.2 TB/s on this
+  // chip against ~5.6 TB/s for whole-KiB reads); position 0 (k_0) comes from halo().
+  CSA_LDS char* kw = (CSA_LDS char*)&kst[wv][0];
+  const unsigned kw_addr = __builtin_amdgcn_readfirstlane((unsigned)(uintptr_t)kw);
+  auto stage_logits = [&](int first, float (&part)[QMAX]) {  // positions first .. first + 31
+    // k rows of positions first + r (position p is row p - 1), clamped to existing rows; the
+    // offsets are taken from the stage's first row so that they stay small for any T
+    const int sb = min(max(first - 1, 0), Tn - 1);
+    const char* sbase = (const char*)(Kh + (size_t)sb * D);
+#pragma unroll
+    for (int c = 0; c < NST; ++c) {
+      const int byte = 1024 * c + 16 * lane;
+      const int r = byte / ROWB, slot = (byte % ROWB) / 16;
+      const int cc = slot ^ (r & (NCH - 1));
+      const int krow_i = min(max(first + r - 1, 0), Tn - 1);  // >= sb
+      lds_copy16(sbase, (krow_i - sb) * ROWB + 16 * cc, kw_addr + 1024 * c);
+    }
+    wait_vmem();
+    asm volatile("" ::: "memory");
+    const int r = lane & 31, h = lane >> 5;
+    float acc[QMAX];
+#pragma unroll
+    for (int j = 0; j < QMAX; ++j) acc[j] = 0.0f;
+#pragma unroll
+    for (int c = 0; c < NCH / 2; ++c) {
+      const int cc = h * (NCH / 2) + c;
+      const f32x4v kc = *(CSA_LDS const f32x4v*)(kw + r * ROWB + 16 * (cc ^ (r & (NCH - 1))));
+#pragma unroll
+      for (int j = 0; j < QMAX; ++j) {
+        if (j < Tq) {
+          const f32x4v qc = *(const f32x4v*)&qs[wv][j][cc * EPC];  // broadcast read
+          if constexpr (F32) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc[j] = __builtin_fmaf(kc[e], qc[e], acc[j]);
+          } else {
+            // whole-chunk bit casts, then element pairs (a bit cast of a single vector
+            // element would read element 0)
+            const bf16x8 kb = __builtin_bit_cast(bf16x8, kc);
+            const bf16x8 qb = __builtin_bit_cast(bf16x8, qc);
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              acc[j] = __builtin_amdgcn_fdot2_f32_bf16(bf16x2v{kb[2 * e], kb[2 * e + 1]},
+                                                       bf16x2v{qb[2 * e], qb[2 * e + 1]}, acc[j], false);
+          }
+        }
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < QMAX; ++j) {  // the two halves of row r: lanes r and r + 32
+      const Half hv = pair_values(acc[j]);
+      part[j] = hv.lo + hv.hi;
+    }
+  };
+  auto logits = [&](int base, float (&a)[QMAX]) {  // positions base + lane
+    float lo[QMAX], hi[QMAX];
+    stage_logits(base, lo);
+    stage_logits(base + 32, hi);
+    const int pos = base + lane;
+#pragma unroll
+    for (int j = 0; j < QMAX; ++j) {
+      const float v = lane < 32 ? lo[j] : hi[j];
+      a[j] = pos >= 1 && pos <= Tn ? v : 0.0f;
+    }
+    if (base == 0) {  // position 0: k_0 (zeros when absent)
+      float a0[QMAX];
+      halo(0, a0);
+#pragma unroll
+      for (int j = 0; j < QMAX; ++j) a[j] = lane == 0 ? a0[j] : a[j];
+    }
+  };
   float m_run[QMAX], l_run[QMAX], O[QMAX][DPL];
 #pragma unroll
   for (int j = 0; j < QMAX; ++j) {
@@ -224,7 +269,7 @@ __global__ void __launch_bounds__(64 * kDecWaves) decode_partial_kernel(DecParam
   }
 
   float acur[QMAX], anxt[QMAX], aleft0[QMAX];
-  logits(p0 + lane, acur);
+  logits(p0, acur);
   halo(p0 - 1, aleft0);  // left neighbour of the split's first position (none at p0 = 0)
 
   for (int b = 0; b < nb; ++b) {
@@ -232,7 +277,7 @@ __global__ void __launch_bounds__(64 * kDecWaves) decode_partial_kernel(DecParam
     const int pos = base + lane;
     float aright63[QMAX];  // right neighbour of lane 63
     if (b + 1 < nb) {
-      logits(pos + 64, anxt);
+      logits(base + 64, anxt);
 #pragma unroll
       for (int j = 0; j < QMAX; ++j)
         aright63[j] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(anxt[j]), 0));

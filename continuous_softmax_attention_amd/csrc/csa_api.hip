@@ -4,6 +4,7 @@
 
 #include "attn16.hpp"
 #include "bwd16.hpp"
+#include "dec16.hpp"
 #include "decode.hpp"
 #include "half16.hpp"
 #include "attn_fwd.hpp"
@@ -131,9 +132,10 @@ extern "C" int csa_decode(const void* q, const void* k, const void* v, const voi
     else if (d == 64) e = csa::launch_decode<float, 64>(p, s);
     else e = csa::launch_decode<float, 128>(p, s);
   } else {
+    // d = 64, 128: both contractions on the matrix cores (dec16.hpp)
     if (d == 16) e = csa::launch_decode<csa::bf16, 16>(p, s);
-    else if (d == 64) e = csa::launch_decode<csa::bf16, 64>(p, s);
-    else e = csa::launch_decode<csa::bf16, 128>(p, s);
+    else if (d == 64) e = csa::launch_decode16<64>(p, s);
+    else e = csa::launch_decode16<128>(p, s);
   }
   return e == hipSuccess ? CSA_OK : CSA_ERR_HIP;
 }

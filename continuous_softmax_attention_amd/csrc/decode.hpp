@@ -1,6 +1,8 @@
 // Decode / few-query forward of continuous softmax attention on gfx950: Tq <= 8 new
 // queries (the last positions T-Tq+1..T of a sequence) against a key/value cache of T
-// positions plus k_0, v_0.
+// positions plus k_0, v_0.  This file's partial kernel serves float32 and d = 16; bf16
+// at d = 64, 128 runs on the matrix cores (dec16.hpp) and shares the merge kernel and
+// the split plan (decode_chunk).
 //
 // Method: J. Su, "Continuous Softmax Attention", eq. (10)-(11); the correction weights
 // use the p-form of attn_fwd.hpp (edge_terms, float32 Taylor branch).  The result of a
@@ -56,14 +58,14 @@ struct DecParams {
   int chunk;       // positions per split (a multiple of 64)
 };
 
-// Positions per split for B*H heads of T cached positions when `cap` waves of the partial
+// Positions (or key rows) per split for B*H heads of `units` of them when `cap` waves of the partial
 // kernel fit on the device at once: every split is one wave, and a wave's time grows with its
 // number of 64-position blocks, so the call takes about rounds x (blocks per split + a fixed
 // cost) -- choose the split length (1 .. 16 blocks) that minimises it.  A fixed length of 256
 // positions put, e.g., 128 heads x 8193 positions into 33 splits per head: 4224 waves for 4096
 // slots, a second round for the last 3% and half the bandwidth.
-inline int decode_chunk(int64_t BH, int64_t T, int64_t cap) {
-  const int64_t blocks = (T + 1 + 63) / 64;
+inline int decode_chunk(int64_t BH, int64_t units, int64_t cap) {
+  const int64_t blocks = (units + 63) / 64;
   int best = 4;
   double best_t = 1e300;
   for (int cb = 1; cb <= 16; ++cb) {
@@ -150,10 +152,11 @@ __global__ void __launch_bounds__(64 * kDecWaves) decode_partial_kernel(DecParam
   const int pend = min(p0 + p.chunk, Tn + 1);  // this split owns positions [p0, pend)
   const int nb = (pend - p0 + 63) / 64;
 
-  // queries of this head into the wave's LDS slice (read back as broadcasts)
+  // queries of this head into the wave's LDS slice (read back as broadcasts); slots past Tq
+  // hold zeros, so their logits and P V sums run unconditionally and stay finite and unused
   {
     const TT* Qg = (const TT*)p.q + (size_t)bh * Tq * D;
-    for (int i = lane; i < Tq * D; i += 64) qs[wv][i / D][i % D] = Qg[i];
+    for (int i = lane; i < QMAX * D; i += 64) qs[wv][i / D][i % D] = i < Tq * D ? Qg[i] : (TT)0.0f;
   }
   const TT* Kh = (const TT*)p.k + (size_t)bh * Tn * D;
   const TT* Vh = (const TT*)p.v + (size_t)bh * Tn * D;
@@ -218,21 +221,19 @@ __global__ void __launch_bounds__(64 * kDecWaves) decode_partial_kernel(DecParam
       const f32x4v kc = *(CSA_LDS const f32x4v*)(kw + r * ROWB + 16 * (cc ^ (r & (NCH - 1))));
 #pragma unroll
       for (int j = 0; j < QMAX; ++j) {
-        if (j < Tq) {
-          const f32x4v qc = *(const f32x4v*)&qs[wv][j][cc * EPC];  // broadcast read
-          if constexpr (F32) {
+        const f32x4v qc = *(const f32x4v*)&qs[wv][j][cc * EPC];  // broadcast read
+        if constexpr (F32) {
 #pragma unroll
-            for (int e = 0; e < 4; ++e) acc[j] = __builtin_fmaf(kc[e], qc[e], acc[j]);
-          } else {
-            // whole-chunk bit casts, then element pairs (a bit cast of a single vector
-            // element would read element 0)
-            const bf16x8 kb = __builtin_bit_cast(bf16x8, kc);
-            const bf16x8 qb = __builtin_bit_cast(bf16x8, qc);
+          for (int e = 0; e < 4; ++e) acc[j] = __builtin_fmaf(kc[e], qc[e], acc[j]);
+        } else {
+          // whole-chunk bit casts, then element pairs (a bit cast of a single vector
+          // element would read element 0)
+          const bf16x8 kb = __builtin_bit_cast(bf16x8, kc);
+          const bf16x8 qb = __builtin_bit_cast(bf16x8, qc);
 #pragma unroll
-            for (int e = 0; e < 4; ++e)
-              acc[j] = __builtin_amdgcn_fdot2_f32_bf16(bf16x2v{kb[2 * e], kb[2 * e + 1]},
-                                                       bf16x2v{qb[2 * e], qb[2 * e + 1]}, acc[j], false);
-          }
+          for (int e = 0; e < 4; ++e)
+            acc[j] = __builtin_amdgcn_fdot2_f32_bf16(bf16x2v{kb[2 * e], kb[2 * e + 1]},
+                                                     bf16x2v{qb[2 * e], qb[2 * e + 1]}, acc[j], false);
         }
       }
     }
@@ -344,12 +345,10 @@ __global__ void __launch_bounds__(64 * kDecWaves) decode_partial_kernel(DecParam
 #pragma unroll
       for (int kk = 0; kk < 16; ++kk) {
 #pragma unroll
-        for (int j = 0; j < QMAX; ++j) {
-          if (j < Tq) {
-            const float s = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wq[j]), kb + kk));
+        for (int j = 0; j < QMAX; ++j) {  // weights of query slots past Tq are 0
+          const float s = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wq[j]), kb + kk));
 #pragma unroll
-            for (int e = 0; e < DPL; ++e) O[j][e] = __builtin_fmaf(s, vv[kk][e], O[j][e]);
-          }
+          for (int e = 0; e < DPL; ++e) O[j][e] = __builtin_fmaf(s, vv[kk][e], O[j][e]);
         }
       }
     }
@@ -459,7 +458,7 @@ inline hipError_t launch_decode(const DecParams& prm_in, hipStream_t stream) {
                   : prm.Tq <= 4 ? decode_blocks_per_cu<TT, D, 4>()
                                 : decode_blocks_per_cu<TT, D, 8>();
   const int64_t cap = (int64_t)(bpc > 0 ? bpc : 1) * kDecWaves * (cus > 0 ? cus : 1);
-  prm.chunk = decode_chunk(prm.BH, prm.T, cap);
+  prm.chunk = decode_chunk(prm.BH, prm.T + 1, cap);
   prm.nsplit = (prm.T + 1 + prm.chunk - 1) / prm.chunk;
   const int items = prm.BH * prm.nsplit;
   const dim3 grid((items + kDecWaves - 1) / kDecWaves), block(64 * kDecWaves);

@@ -79,6 +79,29 @@ def test_bf16_small_head_dims_no_sink(d):
     assert eo <= TOL[torch.bfloat16] and el <= TOL[torch.bfloat16], (eo, el)
 
 
+@pytest.mark.parametrize("sink", ["random", "zero"])
+@pytest.mark.parametrize("T,Tq", [(1, 1), (8, 8), (64, 3), (65, 8), (129, 1), (1000, 5)])
+def test_bf16_d64_lengths_and_queries(T, Tq, sink):
+    q, k, v, k0, v0 = make_decode_inputs("decode", B=1, H=3, Tq=Tq, T=T, d=64, seed=31 * T + Tq, sink=sink)
+    o, lse = _run(q, k, v, k0, v0)
+    o_ref, l_ref = _reference(q, k, v, k0, v0)
+    eo, el = _errs(o, lse, o_ref, l_ref)
+    assert eo <= TOL[torch.bfloat16] and el <= TOL[torch.bfloat16], (eo, el)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("T,Tq", [(3000, 5), (3074, 5), (2049, 8), (2500, 1)])
+def test_many_heads_every_head(T, Tq, d):
+    # enough heads that a split spans several 64-key tiles; T = 3074 puts the last five
+    # queries on both sides of a split boundary when splits are 128 (or 64) rows long
+    q, k, v, k0, v0 = make_decode_inputs("decode", B=4, H=16, Tq=Tq, T=T, d=d, seed=T + d, sink="random")
+    o, lse = _run(q, k, v, k0, v0)
+    o_ref, l_ref = _reference(q, k, v, k0, v0)
+    eo, el = _errs(o, lse, o_ref, l_ref)
+    _report(f"B4 H16 T{T} Tq{Tq} d{d}", eo, el)
+    assert eo <= TOL[torch.bfloat16] and el <= TOL[torch.bfloat16], (eo, el)
+
+
 @pytest.mark.parametrize("q_mult", [4.0, 8.0, 12.0])
 def test_large_logits_copied_sink(q_mult):
     q, k, v, k0, v0 = make_decode_inputs("decode", B=1, H=3, Tq=8, T=1500, seed=9, sink="copy")

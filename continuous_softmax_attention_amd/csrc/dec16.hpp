@@ -128,7 +128,9 @@ __global__ void __launch_bounds__(64 * kDec16Waves, 2) decode16_kernel(DecParams
   };
 
   // ---- K operand registers: block b, step s = row r0 + 16(n >> 2) + 4b + (n & 3) (clamped
-  // to the last row), chunk 4s + g; S^T block b then holds keys 16g + 4b + r in element r
+  // to the last row), chunk 4s + g; S^T block b then holds keys 16g + 4b + r in element r.
+  // Every K row is read once per call: the loads carry the non-temporal hint (measured on the
+  // B16 H8 T8192 cache: 5.6 -> 6.3 TB/s; the same hint on the V copies into LDS lost 9%).
   bf16x8 kreg[4][NSTEP];
   auto load_k = [&](int r0, int nb) {
 #pragma unroll
@@ -136,7 +138,8 @@ __global__ void __launch_bounds__(64 * kDec16Waves, 2) decode16_kernel(DecParams
       if (b < nb) {  // wave-uniform
         const int row = min(r0 + 16 * (n >> 2) + 4 * b + (n & 3), Tn - 1);
 #pragma unroll
-        for (int s = 0; s < NSTEP; ++s) kreg[b][s] = *(const bf16x8*)(Kh + (size_t)row * D + (4 * s + g) * 8);
+        for (int s = 0; s < NSTEP; ++s)
+          kreg[b][s] = __builtin_nontemporal_load((const bf16x8*)(Kh + (size_t)row * D + (4 * s + g) * 8));
       }
     }
     asm volatile("" ::: "memory");  // issued here, not sunk towards their use

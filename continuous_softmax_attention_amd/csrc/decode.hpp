@@ -380,9 +380,14 @@ __global__ void __launch_bounds__(64 * kDecWaves) decode_partial_kernel(DecParam
   }
 }
 
+// One wave per (head, query): the splits' partial results combined with max-rescaled sums,
+// 16 splits per batch with all of a batch's loads issued together (lanes over d for O, every
+// lane reading the splits' m and l), so that a call of up to 16 splits costs one memory round
+// trip; further batches fold into the running (M, L, acc) like an online softmax.
 template <typename TT, int D>
 __global__ void __launch_bounds__(64) decode_merge_kernel(DecParams p) {
   constexpr int DPL = D >= 64 ? D / 64 : 1;
+  constexpr int NB = 16;
   const int lane = threadIdx.x & 63;
   const int item = blockIdx.x;  // (bh, j)
   const int bh = item / p.Tq;
@@ -390,35 +395,36 @@ __global__ void __launch_bounds__(64) decode_merge_kernel(DecParams p) {
   const int ns = p.nsplit;
   const float* src = p.ws + ((size_t)bh * ns * p.Tq + j) * (D + 2);
   const size_t stride = (size_t)p.Tq * (D + 2);  // between splits
-  // split maxima and weight sums with lanes over splits
-  float M = -__builtin_inff();
-  for (int s = lane; s < ns; s += 64) M = fmaxf(M, src[s * stride + D]);
-  M = wave_max(M);
-  float L = 0.0f;
-  for (int s = lane; s < ns; s += 64) {
-    const float ms = src[s * stride + D];
-    L += ms == -__builtin_inff() ? 0.0f : src[s * stride + D + 1] * exp2_fast(ms - M);
-  }
-  L = wave_sum(L);
-  // values with lanes over d; eight splits' loads in flight at a time
-  float acc[DPL];
+  const int dl = min(lane * DPL, D - DPL);        // d elements of this lane (d = 16: lanes >= 16 repeat)
+  float M = -__builtin_inff(), L = 0.0f, acc[DPL];
 #pragma unroll
   for (int e = 0; e < DPL; ++e) acc[e] = 0.0f;
-  for (int s0 = 0; s0 < ns; s0 += 8) {
-    float f[8], x[8][DPL];
+  for (int s0 = 0; s0 < ns; s0 += NB) {
+    float ms[NB], ls[NB], x[NB][DPL];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int s = min(s0 + u, ns - 1);
-      const float* part = src + s * stride;
-      const float ms = part[D];
-      f[u] = (s0 + u < ns && ms != -__builtin_inff()) ? exp2_fast(ms - M) : 0.0f;
+    for (int u = 0; u < NB; ++u) {
+      const float* part = src + (size_t)min(s0 + u, ns - 1) * stride;
+      ms[u] = s0 + u < ns ? part[D] : -__builtin_inff();
+      ls[u] = part[D + 1];
 #pragma unroll
-      for (int e = 0; e < DPL; ++e) x[u][e] = part[min(lane * DPL + e, D - 1)];
+      for (int e = 0; e < DPL; ++e) x[u][e] = part[dl + e];
     }
+    float Mn = M;
 #pragma unroll
-    for (int u = 0; u < 8; ++u)
+    for (int u = 0; u < NB; ++u) Mn = fmaxf(Mn, ms[u]);
+    if (Mn == -__builtin_inff()) continue;  // nothing weighted yet (uniform)
+    const float sc = M == -__builtin_inff() ? 0.0f : exp2_fast(M - Mn);
+    L *= sc;
 #pragma unroll
-      for (int e = 0; e < DPL; ++e) acc[e] = __builtin_fmaf(x[u][e], f[u], acc[e]);
+    for (int e = 0; e < DPL; ++e) acc[e] *= sc;
+#pragma unroll
+    for (int u = 0; u < NB; ++u) {
+      const float f = ms[u] == -__builtin_inff() ? 0.0f : exp2_fast(ms[u] - Mn);
+      L = __builtin_fmaf(ls[u], f, L);
+#pragma unroll
+      for (int e = 0; e < DPL; ++e) acc[e] = __builtin_fmaf(x[u][e], f, acc[e]);
+    }
+    M = Mn;
   }
   const float inv = 1.0f / L;
   TT* o = (TT*)p.out + ((size_t)bh * p.Tq + j) * D;

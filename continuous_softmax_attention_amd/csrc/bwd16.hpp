@@ -127,6 +127,31 @@ __device__ __forceinline__ int tr_layout_at(int r, int cc) {
   return (cc >> 2) * kRegion + r * 64 + 16 * ((cc & 3) ^ (2 * ((r >> 4) & 1)));
 }
 
+// The P / dS buffers of bwd_dkdv: the transposed layout with the chunk position further
+// XORed with bits 2..3 of the row, so that the 16 rows one lane group writes (one 16-byte
+// chunk each) fall on 16 different bank slots (in the plain layout four rows share one).
+__device__ __forceinline__ int ptr_layout_at(int r, int cc) {
+  return (cc >> 2) * kRegion + r * 64 + 16 * ((cc & 3) ^ (2 * ((r >> 4) & 1)) ^ ((r >> 2) & 3));
+}
+// tr_read of such a buffer: row 16g + 8c + 4rd + (n >> 2) has bits 2..3 equal to (2c + rd) & 3,
+// the same in every lane, so each of the four (c, rd) reads takes its own XORed base:
+// pbase[par][k] = vbase[par] ^ 16 k (the added offsets are multiples of 64 bytes).
+__device__ __forceinline__ void ptr_bases(const int (&vbase)[2], int (&pbase)[2][4]) {
+#pragma unroll
+  for (int par = 0; par < 2; ++par)
+#pragma unroll
+    for (int k = 0; k < 4; ++k) pbase[par][k] = vbase[par] ^ (16 * k);
+}
+__device__ __forceinline__ bf16x8 ptr_read(CSA_LDS const char* tile, const int (&pbase)[2][4], int c, int mb) {
+  CSA_LDS const char* a1 = tile + pbase[mb & 1][(2 * c) & 3] + (mb >> 1) * kRegion + 8 * c * 64;
+  CSA_LDS const char* a2 = tile + pbase[mb & 1][(2 * c + 1) & 3] + (mb >> 1) * kRegion + 8 * c * 64 + 4 * 64;
+  const s16x4 r1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((CSA_LDS s16x4*)a1);
+  const s16x4 r2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((CSA_LDS s16x4*)a2);
+  const bf16x4 b1 = __builtin_bit_cast(bf16x4, r1);
+  const bf16x4 b2 = __builtin_bit_cast(bf16x4, r2);
+  return bf16x8{b1[0], b1[1], b1[2], b1[3], b2[0], b2[1], b2[2], b2[3]};
+}
+
 // A operand of S^T for 16-key block b, contraction step s (row layout)
 __device__ __forceinline__ bf16x8 row_read(CSA_LDS const char* tile, int kbase, int s, int b) {
   return *(CSA_LDS const bf16x8*)(tile + kbase + s * kRegion + b * 1024);
@@ -711,8 +736,9 @@ __global__ void __launch_bounds__(512, 2) bwd_dkdv_kernel(BwdParams p) {
   }
 
   const int kbase = row_kbase(n, g);
-  int vbase[2];
+  int vbase[2], pbase[2][4];
   tr_vbase(n, g, vbase);
+  ptr_bases(vbase, pbase);
   const int hoff = n * WT::HROW + 16 * g;
   // this wave's output blocks: 16 d-columns mb, 16-key blocks kc0 .. kc0 + KPW - 1
   const int mb = NMB == 8 ? wave : (wave & 3);
@@ -727,33 +753,41 @@ __global__ void __launch_bounds__(512, 2) bwd_dkdv_kernel(BwdParams p) {
 
   const int i0 = J / kBlockRows;
   const int i1 = (Tn - 1) / kBlockRows;
+  // this wave's query rows of block `it` in registers (the logits' operands) with mu, delta
+  bf16x8 qreg[NSTEP], dreg[NSTEP];
+  float mu_n, delta_n;
+  auto load_rows = [&](int it) {
+    const int rowc = min(it * kBlockRows + 16 * wave + n, Tn - 1);
+#pragma unroll
+    for (int s = 0; s < NSTEP; ++s) {
+      qreg[s] = *(const bf16x8*)(Qg + (size_t)rowc * ROWB + (4 * s + g) * 16);
+      dreg[s] = *(const bf16x8*)(Og + (size_t)rowc * ROWB + (4 * s + g) * 16);
+    }
+    mu_n = ws.mu[(size_t)bh * Tn + rowc];
+    delta_n = ws.delta[(size_t)bh * Tn + rowc];
+  };
+  load_rows(i0);
+  wait_vmem();  // the key block, its halo and the first rows
+  __syncthreads();
+  // Per block: the logits from the registers first; then the copies of the block's Q and dO
+  // tiles (for dK, dV) and the loads of the next block's rows, both in flight during the
+  // VALU work of the gradients (a wait for the rows would otherwise wait for the copies
+  // issued before them as well: loads complete in order).
   for (int it = i0; it <= i1; ++it) {
     const int Q0 = it * kBlockRows;
+    const int qr = Q0 + 16 * wave + n;
+    float s[16], dp[16];
+    f32x4 Hs, Hd;
+    logits_tile<D>(lds, lds + OFF_KH, kbase, hoff, qreg, s, Hs);
+    logits_tile<D>(lds + OFF_V, lds + OFF_VH, kbase, hoff, dreg, dp, Hd);
+    const float mu = mu_n, delta = delta_n;
     // both 64-row halves always (rows past T repeat row T-1): the dK / dV products read
     // all 128 rows, with P = dS = 0 on rows past T
     stage_tile<D>(lds + OFF_Q, Qg, Q0, toff, Tn, wave);
     stage_tile<D>(lds + OFF_Q + TILE, Qg, Q0 + kTile, toff, Tn, wave);
     stage_tile<D>(lds + OFF_DO, Og, Q0, toff, Tn, wave);
     stage_tile<D>(lds + OFF_DO + TILE, Og, Q0 + kTile, toff, Tn, wave);
-
-    const int qr = Q0 + 16 * wave + n;
-    const int rowc = min(qr, Tn - 1);
-    bf16x8 qreg[NSTEP], dreg[NSTEP];
-#pragma unroll
-    for (int s = 0; s < NSTEP; ++s) {
-      qreg[s] = *(const bf16x8*)(Qg + (size_t)rowc * ROWB + (4 * s + g) * 16);
-      dreg[s] = *(const bf16x8*)(Og + (size_t)rowc * ROWB + (4 * s + g) * 16);
-    }
-    const float mu = ws.mu[(size_t)bh * Tn + rowc];
-    const float delta = ws.delta[(size_t)bh * Tn + rowc];
-    if (it == i0) {  // the key block and halo (first iteration only) must have landed
-      wait_vmem();
-      __syncthreads();
-    }
-    float s[16], dp[16];
-    f32x4 Hs, Hd;
-    logits_tile<D>(lds, lds + OFF_KH, kbase, hoff, qreg, s, Hs);
-    logits_tile<D>(lds + OFF_V, lds + OFF_VH, kbase, hoff, dreg, dp, Hd);
+    if (it < i1) load_rows(it + 1);
     float sl, sr, dl, dr;
     neighbours(s, Hs, n, g, sl, sr);
     neighbours(dp, Hd, n, g, dl, dr);
@@ -782,7 +816,7 @@ __global__ void __launch_bounds__(512, 2) bwd_dkdv_kernel(BwdParams p) {
         pv[e] = (bf16)P[8 * h + e];
         dv[e] = (bf16)dS[8 * h + e];
       }
-      const int at = pt_off + tr_layout_at(prow, 2 * g + h);
+      const int at = pt_off + ptr_layout_at(prow, 2 * g + h);
       *(CSA_LDS bf16x8*)(lds + OFF_P + at) = pv;
       *(CSA_LDS bf16x8*)(lds + OFF_DS + at) = dv;
       if constexpr (WRITE_DS) *(bf16x8*)(dst + 16 * h) = dv;
@@ -798,8 +832,8 @@ __global__ void __launch_bounds__(512, 2) bwd_dkdv_kernel(BwdParams p) {
         const bf16x8 ad = tr_read(lds + OFF_DO + st * TILE, vbase, c, mb);
 #pragma unroll
         for (int i = 0; i < KPW; ++i) {
-          const bf16x8 bs = tr_read(lds + OFF_DS + st * (PT / 2), vbase, c, kc0 + i);
-          const bf16x8 bp = tr_read(lds + OFF_P + st * (PT / 2), vbase, c, kc0 + i);
+          const bf16x8 bs = ptr_read(lds + OFF_DS + st * (PT / 2), pbase, c, kc0 + i);
+          const bf16x8 bp = ptr_read(lds + OFF_P + st * (PT / 2), pbase, c, kc0 + i);
           dK[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aq, bs, dK[i], 0, 0, 0);
           dV[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ad, bp, dV[i], 0, 0, 0);
         }

@@ -1,6 +1,7 @@
-// bf16 causal attention forward for gfx950 on 16x16x32 MFMAs, with three weight rules
+// bf16 causal attention forward for gfx950 on 16x16x32 MFMAs, with four weight rules
 // on the identical tiling: continuous softmax attention (kExact), its first-order form
-// (kFirstOrder) and standard softmax attention (kSoftmax).
+// (kFirstOrder), its interval variant [1/2, t + 1/2] (kHalf) and standard softmax
+// attention (kSoftmax).
 //
 // Method: J. Su, "Continuous Softmax Attention", eq. (10)-(11) -- see attn_fwd.hpp
 // for the correction-weight arithmetic ("p-form"), which is shared; the first-order
@@ -58,7 +59,7 @@ constexpr int kWaves16 = 8;  // 8 waves x 16 queries = 128 rows, as kBlockRows
 
 // Weight rule of a launch: standard softmax attention (eq. (12)), continuous softmax
 // attention (eq. (10)-(11)), or its first-order form with b expanded as in eq. (13).
-enum : int { kSoftmax = 0, kExact = 1, kFirstOrder = 2 };
+enum : int { kSoftmax = 0, kExact = 1, kFirstOrder = 2, kHalf = 3 };
 
 // One 16-byte HBM -> LDS copy per lane (global_load_lds_dwordx4): lane i reads
 // base + voff and writes LDS address lds_addr + 16 i (no instruction offset: it would
@@ -103,10 +104,70 @@ __device__ __forceinline__ void edge_yu(float pl, float pr, float y, float u, fl
   L_right = small ? lt : lr;
 }
 
+// Half segments of the interval variant [1/2, t + 1/2] (Problem Statement: the original
+// paper integrates eq. (2) over that interval).  In the forward's units (c^2 e^{a} x the
+// integral, scaled by 2^{-m}; p = 2^{alpha}, alpha = a log2 e - m, c = ln 2), for a segment
+// with endpoint values p_l, p_r, midpoint value p_m = 2^{(alpha_l + alpha_r)/2},
+// y = alpha_r - alpha_l and u = 1/y:
+//   lower half (sigma in [0, 1/2]):  HL = ((c/2) p_m - (p_m - p_l) u) u  (to the right end),
+//                                    HR = c (p_m - p_l) u - HL           (to the left end);
+//   upper half (sigma in [1/2, 1]):  HL' = (c (p_r - p_m/2) - (p_r - p_m) u) u,
+//                                    HR' = c (p_r - p_m) u - HL';
+// below |y| < 0.1 their second-order Taylor forms in x = c y:
+//   HL = c^2 p_l (1/8 + x/24 + x^2/128),   HR = c^2 p_l (3/8 + x/12 + 5 x^2/384),
+//   HL' = c^2 p_l (3/8 + 7x/24 + 15 x^2/128), HR' = c^2 p_l (1/8 + x/12 + 11 x^2/384).
+namespace half {
+
+constexpr float kC = 0.6931471805599453f;   // ln 2
+constexpr float kC2 = 0.4804530139182014f;  // c^2
+constexpr float kY0 = 0.1f;                 // Taylor below |y| < 0.1
+
+// lower half (sigma in [0, 1/2]) of segment (l, r): HR to l, HL to r
+__device__ __forceinline__ void lower_half(float al, float pl, float ar, float& HR, float& HL) {
+  const float y = ar - al;
+  const float pm = exp2_fast(0.5f * (al + ar));
+  const float u = __builtin_amdgcn_rcpf(y);
+  const float dm = pm - pl;
+  const float hl = __builtin_fmaf(0.5f * kC, pm, -dm * u) * u;
+  const float hr = __builtin_fmaf(kC * dm, u, -hl);
+  const float x = kC * y;
+  const float cp = kC2 * pl;
+  const float hlt = cp * __builtin_fmaf(x, __builtin_fmaf(x, 1.0f / 128.0f, 1.0f / 24.0f), 0.125f);
+  const float hrt = cp * __builtin_fmaf(x, __builtin_fmaf(x, 5.0f / 384.0f, 1.0f / 12.0f), 0.375f);
+  const bool small = __builtin_fabsf(y) < kY0;
+  HR = small ? hrt : hr;
+  HL = small ? hlt : hl;
+}
+
+// upper half (sigma in [1/2, 1]) of segment (l, r): HR' to l, HL' to r
+__device__ __forceinline__ void upper_half(float al, float pl, float ar, float pr, float& HR, float& HL) {
+  const float y = ar - al;
+  const float pm = exp2_fast(0.5f * (al + ar));
+  const float u = __builtin_amdgcn_rcpf(y);
+  const float dm = pr - pm;
+  const float hl = __builtin_fmaf(kC, pr - 0.5f * pm, -dm * u) * u;
+  const float hr = __builtin_fmaf(kC * dm, u, -hl);
+  const float x = kC * y;
+  const float cp = kC2 * pl;
+  const float hlt = cp * __builtin_fmaf(x, __builtin_fmaf(x, 15.0f / 128.0f, 7.0f / 24.0f), 0.375f);
+  const float hrt = cp * __builtin_fmaf(x, __builtin_fmaf(x, 11.0f / 384.0f, 1.0f / 12.0f), 0.125f);
+  const bool small = __builtin_fabsf(y) < kY0;
+  HR = small ? hrt : hr;
+  HL = small ? hlt : hl;
+}
+
+}  // namespace half
+
+// kHalf differs from kExact in two places only: position 0 and position 1 share the upper
+// half of segment (0, 1) (first tile), and the query's own position t and position t+1 share
+// the lower half of segment (t, t+1) -- all of it, c^2 p_t / 2, to position t for the last
+// query, whose position T+1 repeats T.  The second is added in the epilogue from two
+// lane-parallel dot products (keys t and t+1) and two value rows, so the key tiles and the
+// diagonal masks are the forward's.
 template <int D, int W>
 __global__ void __launch_bounds__(512, 4) attn16_kernel(FwdParams p) {
   static_assert(D == 16 || D == 64 || D == 128, "head dimension");
-  static_assert(W == kSoftmax || W == kExact || W == kFirstOrder, "weight rule");
+  static_assert(W == kSoftmax || W == kExact || W == kFirstOrder || W == kHalf, "weight rule");
   constexpr bool CSA = W != kSoftmax;  // position 0, halo and neighbour terms
   constexpr int CH = D / 8;                      // 16-byte chunks per row
   constexpr int ROWB = D * 2;                    // bytes per row in HBM
@@ -230,6 +291,31 @@ __global__ void __launch_bounds__(512, 4) attn16_kernel(FwdParams p) {
     }
     a0 = qsum(part);
   }
+  // interval variant: logits of key rows qr (position t) and qr + 1 (position t + 1), for the
+  // lower half of segment (t, t+1) on the diagonal tile; loaded here, in the shadow of the
+  // first tile's copies
+  float a_t = 0.0f, a_t1 = 0.0f;
+  const bool lastq = qr == Tn - 1;
+  if constexpr (W == kHalf) {
+    const bf16* Kh = (const bf16*)p.k + head;
+    const int rt = min(qr, Tn - 1), rn = min(qr + 1, Tn - 1);
+    float pt = 0.0f, pn = 0.0f;
+#pragma unroll
+    for (int s = 0; s < NSTEP; ++s) {
+      if (4 * s + g < CH) {
+        const bf16x8 kt = *(const bf16x8*)(Kh + (size_t)rt * D + (4 * s + g) * 8);
+        const bf16x8 kn = *(const bf16x8*)(Kh + (size_t)rn * D + (4 * s + g) * 8);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          pt = __builtin_fmaf((float)qreg[s][e], (float)kt[e], pt);
+          pn = __builtin_fmaf((float)qreg[s][e], (float)kn[e], pn);
+        }
+      }
+    }
+    a_t = qsum(pt);
+    a_t1 = qsum(pn);
+  }
+  float hl_next = 0.0f;  // interval variant: HL when position t + 1 is the next tile's first key
 
   // ---- LDS read bases
   // K operand (block b, step s): row 16(n >> 2) + 4b + (n & 3), chunk 4s + g (for d = 16,
@@ -331,6 +417,7 @@ __global__ void __launch_bounds__(512, 4) attn16_kernel(FwdParams p) {
       mx = fmaxf(mx, halo);
     }
     if (CSA && first) mx = fmaxf(mx, a0);
+    if (W == kHalf && last && !lastq) mx = fmaxf(mx, a_t1);  // position t + 1 takes a weight
     mx = qmax(mx);
     {
       const float m_new = fmaxf(m_run, mx * kLog2e);
@@ -455,9 +542,24 @@ __global__ void __launch_bounds__(512, 4) attn16_kernel(FwdParams p) {
       if (first) {    // position 0: only its right neighbour (eq. (10), i = 0)
         const float a0l = __builtin_fmaf(a0, kLog2e, -mr);
         float R0, L1;
-        edge_terms<false>(a0l, exp2_fast(a0l), al0, pv0, R0, L1);
+        if constexpr (W == kHalf) half::upper_half(a0l, exp2_fast(a0l), al0, pv0, R0, L1);
+        else edge_terms<false>(a0l, exp2_fast(a0l), al0, pv0, R0, L1);
         w0 = R0;
         if (g == 0) Lprev = L1;
+      }
+      // interval variant, diagonal tile: the lower half of segment (t, t+1) -- HR to the
+      // query's own key (column lim), HL to the next (column lim + 1, or the next tile's
+      // first key when lim = 15 in lane group 3: added in the epilogue)
+      float hR = 0.0f, hL = 0.0f;
+      if constexpr (W == kHalf && last) {
+        const float alt = __builtin_fmaf(a_t, kLog2e, -mr);
+        const float ptv = exp2_fast(alt);
+        half::lower_half(alt, ptv, __builtin_fmaf(a_t1, kLog2e, -mr), hR, hL);
+        if (lastq) {  // position T+1 repeats T: the whole half segment goes to T
+          hR = 0.5f * half::kC2 * ptv;
+          hL = 0.0f;
+        }
+        if (g == 3 && lim == 15) hl_next = hL;
       }
       // edge (t, t+1) needs p_t, p_{t+1}, y_t = alpha_{t+1} - alpha_t and 1/y_t; the
       // values of key t+2 are formed one step ahead
@@ -484,7 +586,10 @@ __global__ void __launch_bounds__(512, 4) attn16_kernel(FwdParams p) {
           } else {  // diagonal tile: column t keeps only its left term, columns > t get 0
             float R, L;
             edge_yu(pc, pn, yc, uc, 0.0f, R, L);
-            w[t] = t < lim ? Lprev + R : (t == lim ? Lprev : 0.0f);
+            if constexpr (W == kHalf)  // plus the lower half of segment (t, t+1)
+              w[t] = t < lim ? Lprev + R : (t == lim ? Lprev + hR : (t == lim + 1 ? hL : 0.0f));
+            else
+              w[t] = t < lim ? Lprev + R : (t == lim ? Lprev : 0.0f);
             Lprev = L;
           }
           pc = pn;
@@ -493,7 +598,10 @@ __global__ void __launch_bounds__(512, 4) attn16_kernel(FwdParams p) {
           an = ann;
           pn = pnn;
         } else {
-          w[15] = last ? (15 < lim ? Lprev + R15 : (15 == lim ? Lprev : 0.0f)) : Lprev + R15;
+          if constexpr (last && W == kHalf)
+            w[15] = 15 < lim ? Lprev + R15 : (15 == lim ? Lprev + hR : (15 == lim + 1 ? hL : 0.0f));
+          else
+            w[15] = last ? (15 < lim ? Lprev + R15 : (15 == lim ? Lprev : 0.0f)) : Lprev + R15;
         }
         slot(t);
       }
@@ -570,6 +678,19 @@ __global__ void __launch_bounds__(512, 4) attn16_kernel(FwdParams p) {
     w0q = from_lane(n, w0);
     l += w0q;
   }
+  if constexpr (W == kHalf) {
+    if (((qw + 15) & 63) == 63) {  // wave-uniform: its last query's t + 1 opens the next tile
+      const float wn = from_lane(48 + n, hl_next);
+      l += wn;
+      const bf16* Vn = (const bf16*)p.v + head + (size_t)min(qr + 1, Tn - 1) * D;
+#pragma unroll
+      for (int mb = 0; mb < NMB; ++mb) {
+        const bf16x4 vn = *(const bf16x4*)(Vn + 16 * mb + 4 * g);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) O[mb][r] = __builtin_fmaf(wn, (float)vn[r], O[mb][r]);
+      }
+    }
+  }
   const float inv = 1.0f / l;
   if (qr < Tn) {
     const bf16* V0 = (CSA && p.v0 != nullptr) ? (const bf16*)p.v0 + (size_t)bh * D : nullptr;
@@ -587,7 +708,7 @@ __global__ void __launch_bounds__(512, 4) attn16_kernel(FwdParams p) {
       *(bf16x4*)(Og + d0) = bf16x4{(bf16)o4[0], (bf16)o4[1], (bf16)o4[2], (bf16)o4[3]};
     }
     if (p.lse != nullptr && g == 0) {
-      const float corr = W == kExact ? 0.7330258411633287f : 0.0f;  // -2 ln(ln 2)
+      const float corr = (W == kExact || W == kHalf) ? 0.7330258411633287f : 0.0f;  // -2 ln(ln 2)
       p.lse[(size_t)bh * Tn + qr] = (m_run + __builtin_amdgcn_logf(l)) * kLn2 + corr;
     }
   }

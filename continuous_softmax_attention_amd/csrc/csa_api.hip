@@ -6,7 +6,6 @@
 #include "bwd16.hpp"
 #include "dec16.hpp"
 #include "decode.hpp"
-#include "half16.hpp"
 #include "attn_fwd.hpp"
 #include "csa.h"
 #include "validate.hpp"
@@ -48,7 +47,7 @@ int validate_half(const void* q, const void* k, const void* v, const void* k0, c
                   int dtype) {
   const int st = csa::validate(q, k, v, k0, v0, out, lse, B, H, T, d, dtype, true);
   if (st != CSA_OK) return st;
-  return dtype == CSA_BF16 && (d == 64 || d == 128) ? CSA_OK : CSA_ERR_UNSUPPORTED;
+  return dtype == CSA_BF16 ? CSA_OK : CSA_ERR_UNSUPPORTED;  // bf16 kernel only
 }
 
 }  // namespace
@@ -99,8 +98,10 @@ extern "C" int csa_forward_half_interval(const void* q, const void* k, const voi
   const int st = validate_half(q, k, v, k0, v0, out, lse, B, H, T, d, dtype);
   if (st != CSA_OK) return st;
   csa::FwdParams p{q, k, v, k0, v0, out, lse, (int)B, (int)H, (int)T, 0};
-  const hipError_t e = d == 64 ? csa::launch_half<64>(p, (hipStream_t)stream)
-                               : csa::launch_half<128>(p, (hipStream_t)stream);
+  hipError_t e;
+  if (d == 16) e = csa::launch_attn16<16, csa::kHalf>(p, (hipStream_t)stream);
+  else if (d == 64) e = csa::launch_attn16<64, csa::kHalf>(p, (hipStream_t)stream);
+  else e = csa::launch_attn16<128, csa::kHalf>(p, (hipStream_t)stream);
   return e == hipSuccess ? CSA_OK : CSA_ERR_HIP;
 }
 

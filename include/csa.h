@@ -123,8 +123,7 @@ int csa_forward_first_order_check(const void* q, const void* k, const void* v, c
  * lse_t the natural log of the denominator integral.
  *
  * Arguments, layouts, ownership and return codes as csa_forward, except that
- * dtype must be CSA_BF16 and d 64 or 128 (anything else returns
- * CSA_ERR_UNSUPPORTED).
+ * dtype must be CSA_BF16 (CSA_F32 returns CSA_ERR_UNSUPPORTED).
  */
 int csa_forward_half_interval(const void* q, const void* k, const void* v, const void* k0,
                               const void* v0, void* out, float* lse, int64_t B, int64_t H,

@@ -151,13 +151,13 @@ def _checkh(**kw):
 
 
 def test_half_interval_check_rules():
-    # same validation as csa_forward; bf16 and d in {64, 128} only
+    # same validation as csa_forward; bf16 only
     assert _checkh() == OK
     assert _checkh(k0=A + 300 * MB, v0=A + 301 * MB, lse=None) == OK
-    for d in (64, 128):
+    for d in (16, 64, 128):
         assert _checkh(d=d) == OK
         assert _checkh(d=d, dtype=csa.CSA_F32) == UNS
-    assert _checkh(d=16) == UNS
+    assert _checkh(d=32) == UNS
     assert _checkh(d=96) == UNS
     assert _checkh(q=None) == INV
     assert _checkh(T=0) == INV
@@ -165,7 +165,7 @@ def test_half_interval_check_rules():
     assert _checkh(v0=A + 301 * MB + 4) == INV
     # the launching entry point rejects the same calls before any HIP call
     assert csa.csa_forward_half_interval_raw(None, A, A, None, None, A + MB, None, 1, 1, 8, 64, csa.CSA_BF16) == INV
-    assert csa.csa_forward_half_interval_raw(A, A + MB, A + 2 * MB, None, None, A + 3 * MB, None, 1, 1, 8, 16,
+    assert csa.csa_forward_half_interval_raw(A, A + MB, A + 2 * MB, None, None, A + 3 * MB, None, 1, 1, 8, 32,
                                              csa.CSA_BF16) == UNS
 
 

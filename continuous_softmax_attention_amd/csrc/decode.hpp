@@ -60,10 +60,13 @@ struct DecParams {
 
 // Positions (or key rows) per split for B*H heads of `units` of them when `cap` waves of the partial
 // kernel fit on the device at once: every split is one wave, and a wave's time grows with its
-// number of 64-position blocks, so the call takes about rounds x (blocks per split + a fixed
-// cost) -- choose the split length (1 .. 16 blocks) that minimises it.  A fixed length of 256
-// positions put, e.g., 128 heads x 8193 positions into 33 splits per head: 4224 waves for 4096
-// slots, a second round for the last 3% and half the bandwidth.
+// number of 64-position blocks, so the partial pass takes about rounds x (blocks per split + a
+// fixed cost); the merge walks a head's splits 16 at a time, one memory round trip each, about a
+// quarter of a block's time (B16 H8 T8192 d128: ~10 us per block round, ~2.5 us per merge
+// batch).  Choose the split length (1 .. 16 blocks) that minimises the sum.  A fixed length of
+// 256 positions put 128 heads x 8193 positions into 33 splits per head: 4224 waves for 4096
+// slots, a second round for the last 3% and half the bandwidth; without the merge term a single
+// head of 131072 positions took 2048 one-block splits and 128 merge batches.
 inline int decode_chunk(int64_t BH, int64_t units, int64_t cap) {
   const int64_t blocks = (units + 63) / 64;
   int best = 4;
@@ -71,7 +74,7 @@ inline int decode_chunk(int64_t BH, int64_t units, int64_t cap) {
   for (int cb = 1; cb <= 16; ++cb) {
     const int64_t ns = (blocks + cb - 1) / cb;
     const int64_t rounds = (BH * ns + cap - 1) / cap;
-    const double t = (double)rounds * (cb + 0.5);
+    const double t = (double)rounds * (cb + 0.5) + 0.25 * (double)((ns + 15) / 16);
     if (t <= best_t) {  // ties: the longer splits (fewer partial results to merge)
       best_t = t;
       best = cb;

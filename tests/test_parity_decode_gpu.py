@@ -102,6 +102,17 @@ def test_many_heads_every_head(T, Tq, d):
     assert eo <= TOL[torch.bfloat16] and el <= TOL[torch.bfloat16], (eo, el)
 
 
+@pytest.mark.parametrize("Tq", [1, 3])
+def test_long_cache_one_head(Tq):
+    # one head of a 131072-position cache: hundreds of splits, merged 16 at a time
+    q, k, v, k0, v0 = make_decode_inputs("decode", B=1, H=1, Tq=Tq, T=131072, seed=40 + Tq, sink="random")
+    o, lse = _run(q, k, v, k0, v0)
+    o_ref, l_ref = _reference(q, k, v, k0, v0)
+    eo, el = _errs(o, lse, o_ref, l_ref)
+    _report(f"one head T131072 Tq{Tq}", eo, el)
+    assert eo <= TOL[torch.bfloat16] and el <= TOL[torch.bfloat16], (eo, el)
+
+
 @pytest.mark.parametrize("q_mult", [4.0, 8.0, 12.0])
 def test_large_logits_copied_sink(q_mult):
     q, k, v, k0, v0 = make_decode_inputs("decode", B=1, H=3, Tq=8, T=1500, seed=9, sink="copy")

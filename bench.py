@@ -22,7 +22,11 @@ its two: S recomputed, dP, dV, dK, dQ).
 
 Prints ONE JSON line.  `cpu_baseline` times the float64 CPU reference on a
 bounded sample of query rows of the same workload (process pool over host
-cores), scaled to TFLOP/s by the same FLOP convention.
+cores), scaled to TFLOP/s by the same FLOP convention.  `mfma_ceiling` runs an
+MFMA-only micro-benchmark (csa_probe in libcsa_bench) on the same GPU: the bf16
+MFMA rate the chip sustains under that load, the shader clock it ran at, and the
+forward's fraction of that rate.  `--probes` prints the full set of SIMD
+micro-benchmarks instead (VALU, exp and rcp issue cost; MFMA and VALU together).
 """
 
 from __future__ import annotations
@@ -170,6 +174,50 @@ def time_kernel(fn, steps, warmup, stream, settle_s=None):
     return sum(per) / len(per), min(per), wall_ms
 
 
+# iterations per probe launch: ~2-3 ms each at four waves per SIMD
+_PROBE_ITERS = {0: 20000, 1: 40000, 2: 20000, 3: 20000, 4: 10000}
+_PROBE_WAVES = 4096  # four per SIMD of the 256 CUs
+
+
+def simd_probes(kinds, stream):
+    """SIMD micro-benchmarks (csa_probe in libcsa_bench), four waves per SIMD: per kind the
+    launch duration and the issue cost per instruction per SIMD; kind 0 gives the MFMA-only
+    ceiling the kernels are compared with.  The shader clock comes from the fp32 FMA kernel
+    (kind 1), whose waves issue round-robin, so that wave 0's s_memtime cycles span the launch
+    (in the MFMA and transcendental kernels the oldest wave runs ahead and finishes early)."""
+    import torch
+
+    import continuous_softmax_attention_amd as csa
+
+    dev = torch.device("cuda:0")
+    sink = torch.empty(_PROBE_WAVES // 4, dtype=torch.float32, device=dev)
+    cyc = torch.zeros(1, dtype=torch.int64, device=dev)
+    per_simd = _PROBE_WAVES / 1024.0  # waves per SIMD
+    ms, cycles = {}, {}
+    for kind in sorted(set(kinds) | {1}):
+        it = _PROBE_ITERS[kind]
+
+        def launch(kind=kind, it=it):
+            st = csa.csa_probe_raw(kind, _PROBE_WAVES, it, sink.data_ptr(), cyc.data_ptr(), stream.cuda_stream)
+            if st != 0:
+                raise RuntimeError(f"csa_probe({kind}) returned {st}")
+
+        _, ms[kind], _ = time_kernel(launch, 3, 2, stream)
+        cycles[kind] = int(cyc.item())
+    ghz = cycles[1] / (ms[1] * 1e-3) / 1e9
+    res = {"shader_clock_ghz": round(ghz, 3)}
+    for kind in kinds:
+        it, t = _PROBE_ITERS[kind], ms[kind] * 1e-3
+        n = {0: 4, 1: 8, 2: 8, 3: 8, 4: 4}[kind]  # instructions of the kind per iteration
+        r = {"ms": round(ms[kind], 4), "cycles_per_instruction": round(t * ghz * 1e9 / (per_simd * it * n), 2)}
+        if kind == 0:
+            r["tflops"] = round(_PROBE_WAVES * it * 4 * 16384.0 / t / 1e12, 1)
+        if kind == 4:
+            r.pop("cycles_per_instruction")
+        res[kind] = r
+    return res
+
+
 def decode_legs(steps, warmup):
     """csa_decode on the decode workloads: HBM bandwidth of the whole call (both launches),
     counting the key/value cache read once (the algorithmic bytes; q, out and lse are
@@ -249,6 +297,23 @@ def counters_mode(w, q, k, v, k0, v0):
     print(json.dumps({"counters_run": w.name, "copy_bytes": 2 * src.numel() * 4}), flush=True)
 
 
+def probes_mode():
+    """All SIMD micro-benchmarks, one JSON line: the MFMA-only ceiling, the issue cost of fp32
+    FMA, exp and rcp, and MFMA with VALU work in the same waves against the two alone."""
+    import torch
+
+    stream = torch.cuda.current_stream(torch.device("cuda:0"))
+    r = simd_probes([0, 1, 2, 3, 4], stream)
+    # the mixed kernel does half the MFMA iterations of kind 0 and half the FMAs of kind 1
+    parts = (0.5 * r[0]["ms"], 0.5 * r[1]["ms"])
+    out = {"probes": "gfx950 SIMD, 4 waves per SIMD, 256 threads per work-group",
+           "shader_clock_ghz": r["shader_clock_ghz"],
+           "mfma_only": r[0], "fma": r[1], "exp": r[2], "rcp": r[3], "mfma_and_fma": r[4],
+           "mix_over_sum_of_parts": round(r[4]["ms"] / sum(parts), 3),
+           "mix_over_larger_part": round(r[4]["ms"] / max(parts), 3)}
+    print(json.dumps(out), flush=True)
+
+
 def main():
     global SETTLE_S
     ap = argparse.ArgumentParser()
@@ -264,6 +329,10 @@ def main():
     ap.add_argument("--no-half-interval", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-backward", action="store_true")
+    ap.add_argument("--probes", action="store_true",
+                    help="print the SIMD micro-benchmarks (MFMA-only ceiling, VALU / exp / rcp issue cost, "
+                         "MFMA and VALU in one wave) as one JSON line and exit")
+    ap.add_argument("--no-ceiling", action="store_true")
     ap.add_argument("--counters", action="store_true",
                     help="for rocprofv3 --pmc passes: one plain device copy of 256 MiB (counter "
                          "calibration), one csa_forward and one std_fwd launch, then exit")
@@ -274,6 +343,9 @@ def main():
               "(independent (batch, head) shards need no communication); run with --gpus 1",
               file=sys.stderr)
         sys.exit(2)
+
+    if args.probes:
+        return probes_mode()
 
     from workloads import WORKLOADS, make_inputs
 
@@ -356,7 +428,7 @@ def main():
         res["first_order"] = {"value": round(f_tflops, 2), "unit": "TFLOP/s", "kernel_ms": round(f_avg, 4),
                               "pct_peak": round(100.0 * f_tflops / peak, 2),
                               "exact_over_first_order": round(tflops / f_tflops, 4)}
-    if not args.no_half_interval and w.dtype == "bf16" and w.d in (64, 128):
+    if not args.no_half_interval and w.dtype == "bf16":
         hout = torch.empty_like(qd)
         hlse = torch.empty_like(lse)
 
@@ -388,6 +460,12 @@ def main():
         del dod, grads, bws
     if not args.no_decode:
         res["decode"] = decode_legs(args.steps, args.warmup)
+    if not args.no_ceiling and w.dtype == "bf16":
+        pr = simd_probes([0], stream)
+        ghz = pr["shader_clock_ghz"]
+        res["mfma_ceiling"] = {"mfma_only_tflops": pr[0]["tflops"], "frac_of_mfma_only": round(tflops / pr[0]["tflops"], 4),
+                               "shader_clock_ghz": ghz, "peak_at_that_clock_tflops": round(4096 * 256 * ghz / 1e3, 1),
+                               "frac_of_peak_at_that_clock": round(tflops / (4096 * 256 * ghz / 1e3), 4)}
     if cpu is not None:
         res["cpu_baseline"] = cpu
     print(json.dumps(res), flush=True)

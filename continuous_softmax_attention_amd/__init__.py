@@ -36,6 +36,7 @@ from ._lib import (  # noqa: F401
     csa_forward_half_interval_check,
     csa_forward_half_interval_raw,
     csa_forward_raw,
+    csa_probe_raw,
     header_functions,
     library_path,
     load,

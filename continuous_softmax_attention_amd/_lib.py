@@ -51,6 +51,7 @@ _SIGS = {
     "csa_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "std_fwd": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, ctypes.c_int, _vp]),
     "std_fwd_check": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, ctypes.c_int]),
+    "csa_probe": (ctypes.c_int, [ctypes.c_int, _i64, _i64, _vp, _vp, _vp]),
 }
 
 _handles: dict[str, ctypes.CDLL] = {}
@@ -166,6 +167,12 @@ def csa_forward_half_interval_check(q, k, v, k0, v0, out, lse, B, H, T, d, dtype
 
 def std_fwd_check(q, k, v, out, lse, B, H, T, d, dtype) -> int:
     return load("libcsa_bench.so").std_fwd_check(q, k, v, out, lse, B, H, T, d, dtype)
+
+
+def csa_probe_raw(kind, waves, iters, sink, cycles, stream=0) -> int:
+    """One SIMD micro-benchmark launch (include/csa_bench.h): kind 0 MFMA, 1 fp32 FMA,
+    2 exp, 3 rcp, 4 MFMA and FMA together; sink and cycles are device addresses."""
+    return load("libcsa_bench.so").csa_probe(kind, waves, iters, sink, cycles, stream or None)
 
 
 # ---------------------------------------------------------------- torch tensors

@@ -29,6 +29,25 @@ int std_fwd(const void* q, const void* k, const void* v, void* out, float* lse, 
 int std_fwd_check(const void* q, const void* k, const void* v, const void* out, const float* lse,
                   int64_t B, int64_t H, int64_t T, int64_t d, int dtype);
 
+/*
+ * csa_probe -- micro-benchmarks of the gfx950 SIMD, for measurement only: the MFMA-only
+ * ceiling the forward kernels are compared with, the issue cost of the VALU instructions
+ * the correction weights are made of, and whether MFMA and VALU work of one SIMD overlap.
+ * One launch of `ceil(waves / 4)` work-groups of 256 threads (four waves) that run `iters`
+ * iterations of a fixed instruction mix in every wave:
+ *   kind 0  4 independent v_mfma_f32_16x16x32_bf16 chains (4 x 16384 FLOP per iteration)
+ *   kind 1  8 independent fp32 FMA chains
+ *   kind 2  8 independent v_exp_f32 chains
+ *   kind 3  8 independent v_rcp_f32 chains
+ *   kind 4  the MFMAs of kind 0 and 16 fp32 FMAs (two rounds of kind 1) per iteration
+ *   sink    device, >= ceil(waves / 4) floats: one result per work-group (keeps the work)
+ *   cycles  device, 1 uint64: shader-clock cycles (s_memtime) wave 0 spent in its loop
+ *   stream  hipStream_t; the caller times the launch (events) and synchronises.
+ * Returns CSA_OK, CSA_ERR_INVALID_ARG (unknown kind, waves < 1 or > 2^24, iters < 1 or > 2^30,
+ * null sink or cycles; checked before any HIP call) or CSA_ERR_HIP.
+ */
+int csa_probe(int kind, int64_t waves, int64_t iters, float* sink, uint64_t* cycles, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

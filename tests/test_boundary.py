@@ -39,7 +39,15 @@ def test_header_declares_the_entry_points():
             "csa_decode", "csa_decode_check", "csa_decode_workspace_bytes",
             "csa_backward", "csa_backward_check", "csa_backward_workspace_bytes",
             "csa_status_string"} <= set(csa.header_functions("csa.h"))
-    assert {"std_fwd", "std_fwd_check"} <= set(csa.header_functions("csa_bench.h"))
+    assert {"std_fwd", "std_fwd_check", "csa_probe"} <= set(csa.header_functions("csa_bench.h"))
+
+
+def test_probe_rejects_bad_arguments_before_launching():
+    # unknown kind, sizes out of range, null buffers: refused before any HIP call
+    for kind, waves, iters, sink, cyc in ((-1, 64, 1, A, A), (5, 64, 1, A, A), (0, 0, 1, A, A),
+                                          (0, 1 << 25, 1, A, A), (0, 64, 0, A, A), (0, 64, 1 << 31, A, A),
+                                          (0, 64, 1, None, A), (0, 64, 1, A, None)):
+        assert csa.csa_probe_raw(kind, waves, iters, sink, cyc) == INV
 
 
 A = 0x10000  # fake, 16-byte-aligned addresses: validation never dereferences them

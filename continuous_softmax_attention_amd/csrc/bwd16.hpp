@@ -697,7 +697,11 @@ __global__ void __launch_bounds__(512, 2) bwd_dkdv_kernel(BwdParams p) {
   constexpr int OFF_V = TILE, OFF_KH = 2 * TILE, OFF_VH = 2 * TILE + HALO, OFF_Q = 2 * TILE + 2 * HALO;
   constexpr int OFF_DO = OFF_Q + 2 * TILE, OFF_P = OFF_DO + 2 * TILE, OFF_DS = OFF_P + PT;
   constexpr int LDS_BYTES = OFF_DS + PT;
-  constexpr int KPW = NMB == 8 ? 4 : 2;  // 16-key output blocks per wave
+  // output blocks per wave: MPW 16-column d-blocks x KPW 16-key blocks (2 x 2 at d = 128: of the
+  // splits of 4 blocks per wave it reads the fewest operands from LDS -- 8 transposed reads per
+  // 32-query step against 10 for 1 x 4)
+  constexpr int MPW = NMB == 8 ? 2 : 1;
+  constexpr int KPW = 2;
   static_assert(D == 64 || D == 128, "head dimension");
 
   __shared__ __attribute__((aligned(1024))) char smem[LDS_BYTES];
@@ -740,12 +744,14 @@ __global__ void __launch_bounds__(512, 2) bwd_dkdv_kernel(BwdParams p) {
   tr_vbase(n, g, vbase);
   ptr_bases(vbase, pbase);
   const int hoff = n * WT::HROW + 16 * g;
-  // this wave's output blocks: 16 d-columns mb, 16-key blocks kc0 .. kc0 + KPW - 1
-  const int mb = NMB == 8 ? wave : (wave & 3);
-  const int kc0 = NMB == 8 ? 0 : 2 * (wave >> 2);
-  f32x4 dK[KPW], dV[KPW];
+  // this wave's output blocks: d-blocks mb0 .. mb0 + MPW - 1, 16-key blocks kc0 .. kc0 + KPW - 1
+  const int mb0 = MPW * (wave & 3);
+  const int kc0 = KPW * (wave >> 2);
+  f32x4 dK[MPW][KPW], dV[MPW][KPW];
 #pragma unroll
-  for (int i = 0; i < KPW; ++i) dK[i] = dV[i] = f32x4{};
+  for (int a = 0; a < MPW; ++a)
+#pragma unroll
+    for (int i = 0; i < KPW; ++i) dK[a][i] = dV[a][i] = f32x4{};
 
   // P / dS rows of this wave in LDS: query tile row 16 wave + n = tile (wave >> 2), row 16 (wave & 3) + n
   const int prow = 16 * (wave & 3) + n;
@@ -828,14 +834,21 @@ __global__ void __launch_bounds__(512, 2) bwd_dkdv_kernel(BwdParams p) {
     for (int st = 0; st < 2; ++st) {
 #pragma unroll
       for (int c = 0; c < 2; ++c) {
-        const bf16x8 aq = tr_read(lds + OFF_Q + st * TILE, vbase, c, mb);
-        const bf16x8 ad = tr_read(lds + OFF_DO + st * TILE, vbase, c, mb);
+        bf16x8 aq[MPW], ad[MPW];
+#pragma unroll
+        for (int a = 0; a < MPW; ++a) {
+          aq[a] = tr_read(lds + OFF_Q + st * TILE, vbase, c, mb0 + a);
+          ad[a] = tr_read(lds + OFF_DO + st * TILE, vbase, c, mb0 + a);
+        }
 #pragma unroll
         for (int i = 0; i < KPW; ++i) {
           const bf16x8 bs = ptr_read(lds + OFF_DS + st * (PT / 2), pbase, c, kc0 + i);
           const bf16x8 bp = ptr_read(lds + OFF_P + st * (PT / 2), pbase, c, kc0 + i);
-          dK[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aq, bs, dK[i], 0, 0, 0);
-          dV[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ad, bp, dV[i], 0, 0, 0);
+#pragma unroll
+          for (int a = 0; a < MPW; ++a) {
+            dK[a][i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aq[a], bs, dK[a][i], 0, 0, 0);
+            dV[a][i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ad[a], bp, dV[a][i], 0, 0, 0);
+          }
         }
       }
     }
@@ -844,14 +857,18 @@ __global__ void __launch_bounds__(512, 2) bwd_dkdv_kernel(BwdParams p) {
 
   // lane (n, g) holds dK^T[16 mb + 4g + r][key 16 kc + n]
 #pragma unroll
-  for (int i = 0; i < KPW; ++i) {
-    const int row = J + 16 * (kc0 + i) + n;
-    if (row < Tn) {
-      const int d0 = 16 * mb + 4 * g;
-      bf16* ok = (bf16*)p.dk + head + (size_t)row * D + d0;
-      bf16* ov = (bf16*)p.dv + head + (size_t)row * D + d0;
-      *(bf16x4*)ok = bf16x4{(bf16)dK[i][0], (bf16)dK[i][1], (bf16)dK[i][2], (bf16)dK[i][3]};
-      *(bf16x4*)ov = bf16x4{(bf16)dV[i][0], (bf16)dV[i][1], (bf16)dV[i][2], (bf16)dV[i][3]};
+  for (int a = 0; a < MPW; ++a) {
+#pragma unroll
+    for (int i = 0; i < KPW; ++i) {
+      const int row = J + 16 * (kc0 + i) + n;
+      if (row < Tn) {
+        const int d0 = 16 * (mb0 + a) + 4 * g;
+        bf16* ok = (bf16*)p.dk + head + (size_t)row * D + d0;
+        bf16* ov = (bf16*)p.dv + head + (size_t)row * D + d0;
+        const f32x4 k4 = dK[a][i], v4 = dV[a][i];
+        *(bf16x4*)ok = bf16x4{(bf16)k4[0], (bf16)k4[1], (bf16)k4[2], (bf16)k4[3]};
+        *(bf16x4*)ov = bf16x4{(bf16)v4[0], (bf16)v4[1], (bf16)v4[2], (bf16)v4[3]};
+      }
     }
   }
 }

@@ -94,14 +94,18 @@ def cpu_baseline(w, q, k, v, k0, v0, heads=64, rows_per_head=320, seed=123):
     positions = sum(done)                      # sum over sampled rows of (t + 1)
     flop = 4.0 * w.d * positions               # same convention as the metric
     total_rows = w.B * w.H * w.T
+    rate = flop / dt
     return {
-        "value": flop / dt / 1e12,
+        "value": rate / 1e12,
         "unit": "TFLOP/s",
         "cores": workers,
         "kind": "oracle",
         "sample": (f"{len(tasks)} of {nheads} heads x {rows_per_head} seeded query rows "
                    f"({len(tasks) * rows_per_head} of {total_rows} rows), float64 eq. (8), "
                    f"{workers} worker processes, {dt:.1f} s wall"),
+        "sample_s": round(dt, 2),
+        # the whole workload at the sampled rate (row cost grows with t + 1, counted in the FLOP)
+        "extrapolated_full_s": round(float(w.flop) / rate, 1),
     }
 
 

@@ -187,8 +187,7 @@ def simd_probes(kinds, stream):
     """SIMD micro-benchmarks (csa_probe in libcsa_bench), four waves per SIMD: per kind the
     launch duration and the issue cost per instruction per SIMD; kind 0 gives the MFMA-only
     ceiling the kernels are compared with.  The shader clock comes from the fp32 FMA kernel
-    (kind 1), whose waves issue round-robin, so that wave 0's s_memtime cycles span the launch
-    (in the MFMA and transcendental kernels the oldest wave runs ahead and finishes early)."""
+    (kind 1): the longest-running wave's s_memtime cycles over the launch's duration."""
     import torch
 
     import continuous_softmax_attention_amd as csa
@@ -202,6 +201,7 @@ def simd_probes(kinds, stream):
         it = _PROBE_ITERS[kind]
 
         def launch(kind=kind, it=it):
+            cyc.zero_()
             st = csa.csa_probe_raw(kind, _PROBE_WAVES, it, sink.data_ptr(), cyc.data_ptr(), stream.cuda_stream)
             if st != 0:
                 raise RuntimeError(f"csa_probe({kind}) returned {st}")
@@ -466,10 +466,7 @@ def main():
         res["decode"] = decode_legs(args.steps, args.warmup)
     if not args.no_ceiling and w.dtype == "bf16":
         pr = simd_probes([0], stream)
-        ghz = pr["shader_clock_ghz"]
-        res["mfma_ceiling"] = {"mfma_only_tflops": pr[0]["tflops"], "frac_of_mfma_only": round(tflops / pr[0]["tflops"], 4),
-                               "shader_clock_ghz": ghz, "peak_at_that_clock_tflops": round(4096 * 256 * ghz / 1e3, 1),
-                               "frac_of_peak_at_that_clock": round(tflops / (4096 * 256 * ghz / 1e3), 4)}
+        res["mfma_ceiling"] = {"mfma_only_tflops": pr[0]["tflops"], "frac_of_mfma_only": round(tflops / pr[0]["tflops"], 4)}
     if cpu is not None:
         res["cpu_baseline"] = cpu
     print(json.dumps(res), flush=True)

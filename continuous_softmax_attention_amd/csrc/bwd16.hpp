@@ -417,8 +417,9 @@ __global__ void __launch_bounds__(512, 2) bwd_dq_kernel(BwdParams p) {
   const int n = lane & 15, g = lane >> 4;
   const int Tn = p.T, BH = p.B * p.H;
   const int nqb = (Tn + kBlockRows - 1) / kBlockRows;
-  const int bh = blockIdx.x % BH;
-  const int qb = nqb - 1 - blockIdx.x / BH;  // longest query blocks first
+  int bh, qrank;
+  xcd_head_order<4>(blockIdx.x, BH, nqb, bh, qrank);  // as the forward
+  const int qb = nqb - 1 - qrank;                     // longest query blocks first
   const int q0 = qb * kBlockRows;
   const int qw = q0 + 16 * wave;
   const int qr = qw + n;
@@ -560,8 +561,9 @@ __global__ void __launch_bounds__(512, 2) bwd_dq_from_ds_kernel(BwdParams p) {
   const int n = lane & 15, g = lane >> 4;
   const int Tn = p.T, BH = p.B * p.H;
   const int nqb = (Tn + kBlockRows - 1) / kBlockRows;
-  const int bh = blockIdx.x % BH;
-  const int qb = nqb - 1 - blockIdx.x / BH;  // longest query blocks first
+  int bh, qrank;
+  xcd_head_order<4>(blockIdx.x, BH, nqb, bh, qrank);  // as the forward
+  const int qb = nqb - 1 - qrank;                     // longest query blocks first
   const int q0 = qb * kBlockRows;
   const int qw = q0 + 16 * wave;
   const int qr = qw + n;
@@ -712,8 +714,10 @@ __global__ void __launch_bounds__(512, 2) bwd_dkdv_kernel(BwdParams p) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n = lane & 15, g = lane >> 4;
   const int Tn = p.T, BH = p.B * p.H;
-  const int bh = blockIdx.x % BH;
-  const int kb = blockIdx.x / BH;  // block 0 (the most queries) first
+  // heads two at a time per XCD, key block 0 (the most queries) first: fetched bytes per lm launch
+  // 1285 -> 458 MB and 1.3% faster (one head at a time: 1% slower)
+  int bh, kb;
+  xcd_head_order<2>(blockIdx.x, BH, (Tn + kTile - 1) / kTile, bh, kb);
   const int J = kb * kTile;
   const BwdWs ws = bwd_ws(p.ws, BH, Tn);
 

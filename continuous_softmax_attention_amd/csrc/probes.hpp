@@ -2,8 +2,9 @@
 // ceiling against which the forward kernels are compared, the issue cost of the VALU
 // instructions their correction weights are made of, and whether MFMA and VALU work of the
 // same SIMD overlap.  Each kernel runs a fixed instruction mix for `iters` iterations in
-// every wave; wave 0 reads the shader clock (s_memtime) around its loop, so that the host can
-// turn event-timed durations into cycles.
+// every wave; every wave reads the shader clock (s_memtime) around its loop and the largest
+// count is kept (the waves of a SIMD do not all run to the end together: the oldest may finish
+// well before the launch does), so that the host can turn event-timed durations into cycles.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -86,7 +87,7 @@ __global__ void __launch_bounds__(kProbeThreads) probe_kernel(int iters, float* 
   for (int k = 0; k < 8; ++k) acc += x[k];
   // one value per work-group (thread 0), so that the loop's results are used
   if (threadIdx.x == 0) sink[blockIdx.x] = acc;
-  if (threadIdx.x == 0 && blockIdx.x == 0) cycles[0] = t1 - t0;
+  if ((threadIdx.x & 63) == 0) atomicMax(cycles, t1 - t0);  // vector atomic; the host zeroes it
 }
 
 inline hipError_t launch_probe(int kind, int64_t waves, int iters, float* sink, unsigned long long* cycles,

@@ -41,7 +41,8 @@ int std_fwd_check(const void* q, const void* k, const void* v, const void* out, 
  *   kind 3  8 independent v_rcp_f32 chains
  *   kind 4  the MFMAs of kind 0 and 16 fp32 FMAs (two rounds of kind 1) per iteration
  *   sink    device, >= ceil(waves / 4) floats: one result per work-group (keeps the work)
- *   cycles  device, 1 uint64: shader-clock cycles (s_memtime) wave 0 spent in its loop
+ *   cycles  device, 1 uint64, zeroed by the caller: raised (atomic max) to the shader-clock
+ *           cycles (s_memtime) of the longest-running wave's loop
  *   stream  hipStream_t; the caller times the launch (events) and synchronises.
  * Returns CSA_OK, CSA_ERR_INVALID_ARG (unknown kind, waves < 1 or > 2^24, iters < 1 or > 2^30,
  * null sink or cycles; checked before any HIP call) or CSA_ERR_HIP.

@@ -179,30 +179,32 @@ def time_kernel(fn, steps, warmup, stream, settle_s=None):
 
 
 # iterations per probe launch: ~2-3 ms each at four waves per SIMD
-_PROBE_ITERS = {0: 20000, 1: 40000, 2: 20000, 3: 20000, 4: 10000}
+_PROBE_ITERS = {0: 20000, 1: 40000, 2: 20000, 3: 20000, 4: 10000, 5: 20000, 6: 10000, 7: 10000, 8: 10000}
+_PROBE_PER_ITER = {0: 4, 1: 8, 2: 8, 3: 8, 5: 2}  # instructions of the kind per iteration
 _PROBE_WAVES = 4096  # four per SIMD of the 256 CUs
 
 
-def simd_probes(kinds, stream):
-    """SIMD micro-benchmarks (csa_probe in libcsa_bench), four waves per SIMD: per kind the
-    launch duration and the issue cost per instruction per SIMD; kind 0 gives the MFMA-only
-    ceiling the kernels are compared with.  The shader clock comes from the fp32 FMA kernel
-    (kind 1): the longest-running wave's s_memtime cycles over the launch's duration."""
+def simd_probes(kinds, stream, waves=_PROBE_WAVES):
+    """SIMD micro-benchmarks (csa_probe in libcsa_bench), `waves` / 1024 waves per SIMD: per
+    kind the launch duration, the issue cost per instruction per SIMD (single-instruction
+    kinds) and the SIMD cycles per wave-iteration; kind 0 gives the MFMA-only ceiling the
+    kernels are compared with.  The shader clock comes from the fp32 FMA kernel (kind 1): the
+    longest-running wave's s_memtime cycles over the launch's duration."""
     import torch
 
     import continuous_softmax_attention_amd as csa
 
     dev = torch.device("cuda:0")
-    sink = torch.empty(_PROBE_WAVES // 4, dtype=torch.float32, device=dev)
+    sink = torch.empty((waves + 3) // 4, dtype=torch.float32, device=dev)
     cyc = torch.zeros(1, dtype=torch.int64, device=dev)
-    per_simd = _PROBE_WAVES / 1024.0  # waves per SIMD
+    per_simd = waves / 1024.0  # waves per SIMD
     ms, cycles = {}, {}
     for kind in sorted(set(kinds) | {1}):
         it = _PROBE_ITERS[kind]
 
         def launch(kind=kind, it=it):
             cyc.zero_()
-            st = csa.csa_probe_raw(kind, _PROBE_WAVES, it, sink.data_ptr(), cyc.data_ptr(), stream.cuda_stream)
+            st = csa.csa_probe_raw(kind, waves, it, sink.data_ptr(), cyc.data_ptr(), stream.cuda_stream)
             if st != 0:
                 raise RuntimeError(f"csa_probe({kind}) returned {st}")
 
@@ -212,12 +214,11 @@ def simd_probes(kinds, stream):
     res = {"shader_clock_ghz": round(ghz, 3)}
     for kind in kinds:
         it, t = _PROBE_ITERS[kind], ms[kind] * 1e-3
-        n = {0: 4, 1: 8, 2: 8, 3: 8, 4: 4}[kind]  # instructions of the kind per iteration
-        r = {"ms": round(ms[kind], 4), "cycles_per_instruction": round(t * ghz * 1e9 / (per_simd * it * n), 2)}
-        if kind == 0:
-            r["tflops"] = round(_PROBE_WAVES * it * 4 * 16384.0 / t / 1e12, 1)
-        if kind == 4:
-            r.pop("cycles_per_instruction")
+        r = {"ms": round(ms[kind], 4), "cycles_per_wave_iteration": round(t * ghz * 1e9 / (per_simd * it), 1)}
+        if kind in _PROBE_PER_ITER:
+            r["cycles_per_instruction"] = round(t * ghz * 1e9 / (per_simd * it * _PROBE_PER_ITER[kind]), 2)
+        if kind in (0, 5):
+            r["tflops"] = round(waves * it * 65536.0 / t / 1e12, 1)
         res[kind] = r
     return res
 
@@ -302,19 +303,32 @@ def counters_mode(w, q, k, v, k0, v0):
 
 
 def probes_mode():
-    """All SIMD micro-benchmarks, one JSON line: the MFMA-only ceiling, the issue cost of fp32
-    FMA, exp and rcp, and MFMA with VALU work in the same waves against the two alone."""
+    """All SIMD micro-benchmarks, one JSON line: the MFMA-only ceiling (16x16x32 and 32x32x16),
+    the issue cost of fp32 FMA, exp and rcp, MFMA with VALU work in the same waves against the
+    two alone, and the forward's per-key weight arithmetic alone and beside 16x16x32 or
+    32x32x16 MFMAs at the forward's ratio, at 2, 4 and 8 waves per SIMD (the tiling choice)."""
     import torch
 
     stream = torch.cuda.current_stream(torch.device("cuda:0"))
-    r = simd_probes([0, 1, 2, 3, 4], stream)
+    r = simd_probes([0, 1, 2, 3, 4, 5], stream)
     # the mixed kernel does half the MFMA iterations of kind 0 and half the FMAs of kind 1
     parts = (0.5 * r[0]["ms"], 0.5 * r[1]["ms"])
     out = {"probes": "gfx950 SIMD, 4 waves per SIMD, 256 threads per work-group",
            "shader_clock_ghz": r["shader_clock_ghz"],
            "mfma_only": r[0], "fma": r[1], "exp": r[2], "rcp": r[3], "mfma_and_fma": r[4],
            "mix_over_sum_of_parts": round(r[4]["ms"] / sum(parts), 3),
-           "mix_over_larger_part": round(r[4]["ms"] / max(parts), 3)}
+           "mix_over_larger_part": round(r[4]["ms"] / max(parts), 3),
+           "mfma32_only": r[5]}
+    # weight arithmetic (2 keys per wave-iteration) with 4 16x16x32 or 2 32x32x16 MFMAs
+    tiling = {}
+    for wps in (2, 4, 8):
+        w = simd_probes([6, 7, 8], stream, waves=1024 * wps)
+        tiling[f"{wps}_waves_per_simd"] = {
+            "cycles_per_wave_iteration": {"weights": w[6]["cycles_per_wave_iteration"],
+                                          "weights_mfma16x16x32": w[7]["cycles_per_wave_iteration"],
+                                          "weights_mfma32x32x16": w[8]["cycles_per_wave_iteration"]},
+            "mfma32_over_mfma16": round(w[8]["ms"] / w[7]["ms"], 3)}
+    out["weights_and_mfma"] = tiling
     print(json.dumps(out), flush=True)
 
 

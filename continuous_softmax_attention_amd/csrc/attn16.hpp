@@ -10,10 +10,12 @@
 //
 // Why a second tiling.  With 32 queries per wave (32x32 MFMAs) the accumulator of
 // O^T alone takes 64 VGPRs and the kernel needs ~244, which caps the SIMD at two
-// waves; the correction weights are VALU work, a wave issues at most one VALU
-// instruction every 4 cycles and a second wave is needed to fill the other issue
-// slot, so latency (exp/rcp, LDS, MFMA results, barriers) goes unhidden.  Here a
-// wave owns 16 queries: O^T is 32 VGPRs, Q 16, S 16, and four waves fit per SIMD.
+// waves; the correction weights are VALU work whose latency (exp/rcp, LDS, MFMA
+// results, barriers) and VALU dual issue need other waves.  Here a wave owns 16
+// queries: O^T is 32 VGPRs, Q 16, S 16, and four waves fit per SIMD.  Measured with
+// the per-key weight arithmetic beside the MFMAs of this ratio (csa_probe kinds 7 and
+// 8): the 32x32x16 shape is 2% faster than 16x16x32 at equal occupancy, but two
+// waves per SIMD on it take 7% longer than four on 16x16x32 for the same work.
 //
 // Work decomposition
 //   * One work-group = 8 waves = 128 query rows of one (b, h); wave w owns rows

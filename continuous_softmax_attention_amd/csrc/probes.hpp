@@ -1,24 +1,40 @@
 // Micro-benchmarks of the gfx950 SIMD, for measurement only (libcsa_bench): the MFMA-only
 // ceiling against which the forward kernels are compared, the issue cost of the VALU
-// instructions their correction weights are made of, and whether MFMA and VALU work of the
-// same SIMD overlap.  Each kernel runs a fixed instruction mix for `iters` iterations in
-// every wave; every wave reads the shader clock (s_memtime) around its loop and the largest
-// count is kept (the waves of a SIMD do not all run to the end together: the oldest may finish
-// well before the launch does), so that the host can turn event-timed durations into cycles.
+// instructions their correction weights are made of, whether MFMA and VALU work of the
+// same SIMD overlap, and the forward's per-key weight arithmetic beside 16x16x32 or 32x32x16
+// MFMAs at the forward's ratio (the choice of tiling).  Each kernel runs a fixed instruction
+// mix for `iters` iterations in every wave; every wave reads the shader clock (s_memtime)
+// around its loop and the largest count is kept (the waves of a SIMD do not all run to the
+// end together: the oldest may finish well before the launch does), so that the host can turn
+// event-timed durations into cycles.
 #pragma once
 
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
 
+#include "attn16.hpp"
+
 namespace csa {
 
-enum : int { kProbeMfma = 0, kProbeFma = 1, kProbeExp = 2, kProbeRcp = 3, kProbeMix = 4, kProbeKinds = 5 };
+enum : int {
+  kProbeMfma = 0,
+  kProbeFma = 1,
+  kProbeExp = 2,
+  kProbeRcp = 3,
+  kProbeMix = 4,
+  kProbeMfma32 = 5,
+  kProbeWeights = 6,
+  kProbeWeightsMfma = 7,
+  kProbeWeightsMfma32 = 8,
+  kProbeKinds = 9
+};
 constexpr int kProbeThreads = 256;  // four waves per work-group
 
 namespace probe {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 // c += a b on a 16x16x32 bf16 MFMA with the accumulator in the same registers before and
 // after: the builtin in a loop got a different destination than its source for some chains
@@ -29,6 +45,9 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ void mfma_acc(f32x4& c, const bf16x8& a, const bf16x8& b) {
   asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+v"(c) : "v"(a), "v"(b));
 }
+__device__ __forceinline__ void mfma32_acc(f32x16& c, const bf16x8& a, const bf16x8& b) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(c) : "v"(a), "v"(b));
+}
 #pragma clang diagnostic pop
 }  // namespace probe
 
@@ -36,6 +55,12 @@ __device__ __forceinline__ void mfma_acc(f32x4& c, const bf16x8& a, const bf16x8
 // kProbeFma: 8 independent fp32 FMA chains.  kProbeExp / kProbeRcp: 8 independent v_exp_f32 /
 // v_rcp_f32 chains (exp2 of the negated value and the reciprocal keep every chain bounded).
 // kProbeMix: the MFMAs of kProbeMfma and two rounds of the FMAs of kProbeFma per iteration.
+// kProbeMfma32: 2 independent v_mfma_f32_32x32x16_bf16 chains (32768 FLOP each), the FLOP of
+// kProbeMfma.  kProbeWeights: the forward's arithmetic for two keys per iteration (logit to
+// alpha, exp2, neighbour difference, reciprocal, edge_yu with its Taylor select) on two
+// interleaved chains of logits that wander in [-3, 3).  kProbeWeightsMfma / kProbeWeightsMfma32:
+// kProbeWeights with the MFMAs of kProbeMfma / kProbeMfma32 -- two 16x16x32 MFMAs per key and
+// lane, the forward's ratio (32 per 16 x 64 wave-tile).
 template <int KIND>
 __global__ void __launch_bounds__(kProbeThreads) probe_kernel(int iters, float* sink, unsigned long long* cycles) {
   using probe::bf16x8;
@@ -52,17 +77,49 @@ __global__ void __launch_bounds__(kProbeThreads) probe_kernel(int iters, float* 
   b2[1] = (__bf16)1.0f;
   b3[2] = (__bf16)1.0f;
   f32x4 c0 = {}, c1 = {}, c2 = {}, c3 = {};
+  f32x16 e0 = {}, e1 = {};
+  constexpr bool M16 = KIND == kProbeMfma || KIND == kProbeMix || KIND == kProbeWeightsMfma;
+  constexpr bool M32 = KIND == kProbeMfma32 || KIND == kProbeWeightsMfma32;
+  constexpr bool WGT = KIND == kProbeWeights || KIND == kProbeWeightsMfma || KIND == kProbeWeightsMfma32;
+  float sv[2], ap[2], pc[2], lp[2], wsum[2];  // weight chains: logit, alpha, p, left term, sum
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    sv[k] = 0.3f * (float)((lane + k) & 7);
+    ap[k] = -1.0f;
+    pc[k] = 0.5f;
+    lp[k] = 0.0f;
+    wsum[k] = 0.0f;
+  }
   float x[8];
 #pragma unroll
   for (int k = 0; k < 8; ++k) x[k] = 0.5f + 0.01f * (float)((lane + k) & 15);
   const float m = 0.999f + 1e-6f * (float)lane, s = 1e-3f * (float)(lane & 7);
   const unsigned long long t0 = __builtin_amdgcn_s_memtime();
   for (int i = 0; i < iters; ++i) {
-    if constexpr (KIND == kProbeMfma || KIND == kProbeMix) {
+    if constexpr (M16) {
       probe::mfma_acc(c0, a, b);
       probe::mfma_acc(c1, a, b1);
       probe::mfma_acc(c2, a, b2);
       probe::mfma_acc(c3, a, b3);
+    }
+    if constexpr (M32) {
+      probe::mfma32_acc(e0, a, b);
+      probe::mfma32_acc(e1, a, b1);
+    }
+    if constexpr (WGT) {
+#pragma unroll
+      for (int k = 0; k < 2; ++k) {
+        float v = __builtin_fmaf(sv[k], m, 0.37f);
+        sv[k] = v >= 3.0f ? v - 6.0f : v;
+        const float al = __builtin_fmaf(sv[k], kLog2e, -2.0f);
+        const float pn = __builtin_amdgcn_exp2f(al);
+        const float y = al - ap[k];
+        float w;
+        edge_yu(pc[k], pn, y, __builtin_amdgcn_rcpf(y), lp[k], w, lp[k]);
+        wsum[k] += w;
+        pc[k] = pn;
+        ap[k] = al;
+      }
     }
     if constexpr (KIND == kProbeFma || KIND == kProbeMix) {
 #pragma unroll
@@ -83,6 +140,10 @@ __global__ void __launch_bounds__(kProbeThreads) probe_kernel(int iters, float* 
   float acc = 0.0f;
   const f32x4 csum = c0 + c1 + c2 + c3;
   acc += csum[0] + csum[1] + csum[2] + csum[3];
+  const f32x16 esum = e0 + e1;
+#pragma unroll
+  for (int k = 0; k < 16; ++k) acc += esum[k];
+  acc += wsum[0] + wsum[1];
 #pragma unroll
   for (int k = 0; k < 8; ++k) acc += x[k];
   // one value per work-group (thread 0), so that the loop's results are used
@@ -98,7 +159,15 @@ inline hipError_t launch_probe(int kind, int64_t waves, int iters, float* sink, 
     case kProbeFma: hipLaunchKernelGGL((probe_kernel<kProbeFma>), grid, block, 0, stream, iters, sink, cycles); break;
     case kProbeExp: hipLaunchKernelGGL((probe_kernel<kProbeExp>), grid, block, 0, stream, iters, sink, cycles); break;
     case kProbeRcp: hipLaunchKernelGGL((probe_kernel<kProbeRcp>), grid, block, 0, stream, iters, sink, cycles); break;
-    default: hipLaunchKernelGGL((probe_kernel<kProbeMix>), grid, block, 0, stream, iters, sink, cycles); break;
+    case kProbeMix: hipLaunchKernelGGL((probe_kernel<kProbeMix>), grid, block, 0, stream, iters, sink, cycles); break;
+    case kProbeMfma32: hipLaunchKernelGGL((probe_kernel<kProbeMfma32>), grid, block, 0, stream, iters, sink, cycles); break;
+    case kProbeWeights: hipLaunchKernelGGL((probe_kernel<kProbeWeights>), grid, block, 0, stream, iters, sink, cycles); break;
+    case kProbeWeightsMfma:
+      hipLaunchKernelGGL((probe_kernel<kProbeWeightsMfma>), grid, block, 0, stream, iters, sink, cycles);
+      break;
+    default:
+      hipLaunchKernelGGL((probe_kernel<kProbeWeightsMfma32>), grid, block, 0, stream, iters, sink, cycles);
+      break;
   }
   return hipGetLastError();
 }

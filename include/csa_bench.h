@@ -32,7 +32,8 @@ int std_fwd_check(const void* q, const void* k, const void* v, const void* out, 
 /*
  * csa_probe -- micro-benchmarks of the gfx950 SIMD, for measurement only: the MFMA-only
  * ceiling the forward kernels are compared with, the issue cost of the VALU instructions
- * the correction weights are made of, and whether MFMA and VALU work of one SIMD overlap.
+ * the correction weights are made of, whether MFMA and VALU work of one SIMD overlap, and
+ * the forward's weight arithmetic beside either MFMA shape (the choice of tiling).
  * One launch of `ceil(waves / 4)` work-groups of 256 threads (four waves) that run `iters`
  * iterations of a fixed instruction mix in every wave:
  *   kind 0  4 independent v_mfma_f32_16x16x32_bf16 chains (4 x 16384 FLOP per iteration)
@@ -40,6 +41,11 @@ int std_fwd_check(const void* q, const void* k, const void* v, const void* out, 
  *   kind 2  8 independent v_exp_f32 chains
  *   kind 3  8 independent v_rcp_f32 chains
  *   kind 4  the MFMAs of kind 0 and 16 fp32 FMAs (two rounds of kind 1) per iteration
+ *   kind 5  2 independent v_mfma_f32_32x32x16_bf16 chains (2 x 32768 FLOP per iteration)
+ *   kind 6  the forward's correction-weight arithmetic for two keys per iteration (exp2,
+ *           neighbour difference, reciprocal, both edge terms with the Taylor select)
+ *   kind 7  kinds 6 and 0 together (two 16x16x32 MFMAs per key, the forward's ratio)
+ *   kind 8  kinds 6 and 5 together (the same FLOP on 32x32x16 MFMAs)
  *   sink    device, >= ceil(waves / 4) floats: one result per work-group (keeps the work)
  *   cycles  device, 1 uint64, zeroed by the caller: raised (atomic max) to the shader-clock
  *           cycles (s_memtime) of the longest-running wave's loop

@@ -444,13 +444,14 @@ __global__ void __launch_bounds__(512, 4) attn16_kernel(FwdParams p) {
     }
     if (CSA && first) mx = fmaxf(mx, a0);
     if (W == kHalf && last && !lastq) mx = fmaxf(mx, a_t1);  // position t + 1 takes a weight
-    mx = qmax(mx);
-    {
-      const float m_new = fmaxf(m_run, mx * kLog2e);
-      if (__builtin_amdgcn_ballot_w64(m_new > m_run + 8.0f) != 0) {
-        rescale_all(exp2_fast(m_run - m_new));
-        m_run = m_new;
-      }
+    // the shift moves only if some lane's own maximum passes m_run + 8 (the same test as on
+    // the query-wide maximum, which is the largest of its lanes'); only then the maximum over
+    // the query's four lanes, and every query of the wave takes its new shift (unchanged
+    // where it did not grow: factor exactly 1)
+    if (__builtin_amdgcn_ballot_w64(mx * kLog2e > m_run + 8.0f) != 0) {
+      const float m_new = fmaxf(m_run, qmax(mx) * kLog2e);
+      rescale_all(exp2_fast(m_run - m_new));
+      m_run = m_new;
     }
     float mr = m_run;
     asm volatile("" : "+v"(mr));  // each path keeps its own exponentials

@@ -84,6 +84,17 @@ def test_edge_shapes_with_random_sink(T, d):
     _compare(f"T{T} d{d}", got, ref)
 
 
+@pytest.mark.parametrize("B,H,T,d", [(2, 16, 200, 128), (1, 16, 130, 64)])
+def test_head_groups_per_xcd(B, H, T, d):
+    # B*H = 32: the dq kernels take the XCD-grouped order (four heads at a time) and bwd_dkdv
+    # its grouping by two; B*H = 16: bwd_dkdv grouped, the dq kernels in plain order
+    print(f"[backward] B{B} H{H} T{T} d{d} (grouped work-group order)", flush=True)
+    q, k, v, k0, v0, do = _random_case(B, H, T, d, seed=500 + T + d)
+    got = _run(q, k, v, k0, v0, do)
+    ref = csa_backward_reference(q, k, v, do, k0, v0)
+    _compare(f"B{B} H{H} T{T} d{d}", got, ref)
+
+
 def test_many_heads_no_sink():
     # k0 = v0 = 0: dk0, dv0 are the gradient at the zero vector
     print("[backward] B2 H3 T300 d128 no sink", flush=True)

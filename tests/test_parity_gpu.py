@@ -82,6 +82,19 @@ def test_many_heads_not_multiple_of_eight():
     assert eo <= 2e-2 and el <= 2e-2
 
 
+@pytest.mark.parametrize("d", [64, 128])
+def test_head_groups_per_xcd(d):
+    # B*H a multiple of 32: work-groups take the XCD-grouped order (four heads per XCD at a
+    # time, query blocks longest first), here with a ragged last query block
+    print(f"[parity] B2 H16 T300 d{d} bf16 (grouped work-group order)", flush=True)
+    q, k, v, k0, v0 = _random_case(2, 16, 300, d, torch.bfloat16, seed=77 + d)
+    o, lse = _run(q, k, v, k0, v0)
+    o_ref, l_ref = csa_reference(q, k, v, k0, v0)
+    eo, el = _errs(o, lse, o_ref, l_ref)
+    _report(f"B2 H16 T300 d{d} bf16", eo, el)
+    assert eo <= 2e-2 and el <= 2e-2
+
+
 # float32 logits of size ~40 carry ~|a| 2^-24 absolute rounding each, so at logit
 # std 8 the float32 bar is 4e-5 instead of the 1e-5 of unit-scale workloads.
 LARGE_TOL = {torch.float32: 4e-5, torch.bfloat16: 2e-2}

@@ -86,8 +86,8 @@ def test_edge_shapes_with_random_sink(T, d):
 
 @pytest.mark.parametrize("B,H,T,d", [(2, 16, 200, 128), (1, 16, 130, 64)])
 def test_head_groups_per_xcd(B, H, T, d):
-    # B*H = 32: the dq kernels take the XCD-grouped order (four heads at a time) and bwd_dkdv
-    # its grouping by two; B*H = 16: bwd_dkdv grouped, the dq kernels in plain order
+    # B*H = 32: every backward kernel takes the XCD-grouped order (four heads at a time per
+    # XCD); B*H = 16: the plain heads-fastest order
     print(f"[backward] B{B} H{H} T{T} d{d} (grouped work-group order)", flush=True)
     q, k, v, k0, v0, do = _random_case(B, H, T, d, seed=500 + T + d)
     got = _run(q, k, v, k0, v0, do)

@@ -13,7 +13,9 @@ to softmax attention with a neighbour-dependent correction (eq. (10)-(11)).
 from ._lib import (  # noqa: F401
     CSA_BF16,
     CSA_ERR_HIP,
+    CSA_DECODE_NOALLOC_SCRATCH_BYTES,
     CSA_ERR_INVALID_ARG,
+    CSA_ERR_SCRATCH_TOO_SMALL,
     CSA_ERR_UNSUPPORTED,
     CSA_F32,
     CSA_OK,
@@ -25,6 +27,9 @@ from ._lib import (  # noqa: F401
     csa_backward_workspace_bytes_fast,
     csa_decode,
     csa_decode_check,
+    csa_decode_noalloc,
+    csa_decode_noalloc_check,
+    csa_decode_noalloc_raw,
     csa_decode_raw,
     csa_decode_workspace_bytes,
     csa_forward,

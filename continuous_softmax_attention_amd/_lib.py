@@ -22,6 +22,8 @@ CSA_OK = 0
 CSA_ERR_INVALID_ARG = 1
 CSA_ERR_UNSUPPORTED = 2
 CSA_ERR_HIP = 3
+CSA_ERR_SCRATCH_TOO_SMALL = 4
+CSA_DECODE_NOALLOC_SCRATCH_BYTES = 64 << 20  # the static scratch of csa_decode_noalloc (include/csa.h)
 
 
 class CsaError(RuntimeError):
@@ -44,6 +46,8 @@ _SIGS = {
     "csa_decode_check": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64, _i64,
                                         ctypes.c_int]),
     "csa_decode_workspace_bytes": (_i64, [_i64, _i64, _i64, _i64, _i64]),
+    "csa_decode_noalloc": (ctypes.c_int, [_vp] * 7 + [_i64] * 5 + [ctypes.c_int, _vp]),
+    "csa_decode_noalloc_check": (ctypes.c_int, [_vp] * 7 + [_i64] * 5 + [ctypes.c_int]),
     "csa_backward": (ctypes.c_int, [_vp] * 14 + [_i64] * 5 + [ctypes.c_int, _vp]),
     "csa_backward_check": (ctypes.c_int, [_vp] * 14 + [_i64] * 5 + [ctypes.c_int]),
     "csa_backward_workspace_bytes": (_i64, [_i64] * 4),
@@ -92,7 +96,8 @@ def status_string(status: int) -> str:
     try:
         return load().csa_status_string(int(status)).decode()
     except Exception:  # library missing: still give a readable message
-        return {0: "ok", 1: "invalid argument", 2: "unsupported", 3: "HIP launch failure"}.get(status, "unknown")
+        return {0: "ok", 1: "invalid argument", 2: "unsupported", 3: "HIP launch failure",
+                4: "sizes exceed the static decode scratch"}.get(status, "unknown")
 
 
 # ---------------------------------------------------------------- raw pointers
@@ -119,6 +124,15 @@ def csa_decode_raw(q, k, v, k0, v0, out, lse, ws, ws_bytes, B, H, Tq, T, d, dtyp
 
 def csa_decode_check(q, k, v, k0, v0, out, lse, ws, ws_bytes, B, H, Tq, T, d, dtype) -> int:
     return load().csa_decode_check(q, k, v, k0, v0, out, lse, ws, ws_bytes, B, H, Tq, T, d, dtype)
+
+
+def csa_decode_noalloc_raw(q, k, v, k0, v0, out, lse, B, H, Tq, T, d, dtype, stream=0) -> int:
+    return load().csa_decode_noalloc(q, k, v, k0 or None, v0 or None, out, lse or None, B, H, Tq, T, d, dtype,
+                                     stream or None)
+
+
+def csa_decode_noalloc_check(q, k, v, k0, v0, out, lse, B, H, Tq, T, d, dtype) -> int:
+    return load().csa_decode_noalloc_check(q, k, v, k0, v0, out, lse, B, H, Tq, T, d, dtype)
 
 
 def csa_decode_workspace_bytes(B, H, Tq, T, d) -> int:
@@ -287,6 +301,33 @@ def std_fwd(q, k, v, *, out=None, lse=None, return_lse=True, stream=None):
     return out, lse
 
 
+def _decode_args(q, k, v, k0, v0, out, lse, return_lse, what):
+    import torch
+
+    if q.dim() != 4 or k.dim() != 4:
+        raise ValueError("q must be [B, H, Tq, d] and k, v [B, H, T, d]")
+    B, H, Tq, d = q.shape
+    T = k.shape[2]
+    dt, dev = q.dtype, q.device
+    if dev.type != "cuda":
+        raise ValueError(f"{what} runs on the GPU only; inputs must be device tensors")
+    _check("q", q, (B, H, Tq, d), dt, dev)
+    for name, t in (("k", k), ("v", v)):
+        _check(name, t, (B, H, T, d), dt, dev)
+    for name, t in (("k0", k0), ("v0", v0)):
+        if t is not None:
+            _check(name, t, (B, H, d), dt, dev)
+    if out is None:
+        out = torch.empty_like(q)
+    else:
+        _check("out", out, (B, H, Tq, d), dt, dev)
+    if lse is None and return_lse:
+        lse = torch.empty((B, H, Tq), dtype=torch.float32, device=dev)
+    elif lse is not None:
+        _check("lse", lse, (B, H, Tq), torch.float32, dev)
+    return B, H, Tq, T, d, out, lse
+
+
 def csa_decode(q, k, v, k0=None, v0=None, *, out=None, lse=None, return_lse=True, workspace=None, stream=None):
     """Forward of a few new queries against a key/value cache through libcsa.
 
@@ -297,40 +338,36 @@ def csa_decode(q, k, v, k0=None, v0=None, *, out=None, lse=None, return_lse=True
     """
     import torch
 
-    if q.dim() != 4 or k.dim() != 4:
-        raise ValueError("q must be [B, H, Tq, d] and k, v [B, H, T, d]")
-    B, H, Tq, d = q.shape
-    T = k.shape[2]
-    dt, dev = q.dtype, q.device
-    if dev.type != "cuda":
-        raise ValueError("csa_decode runs on the GPU only; inputs must be device tensors")
-    _check("q", q, (B, H, Tq, d), dt, dev)
-    for name, t in (("k", k), ("v", v)):
-        _check(name, t, (B, H, T, d), dt, dev)
-    for name, t in (("k0", k0), ("v0", v0)):
-        if t is not None:
-            _check(name, t, (B, H, d), dt, dev)
+    B, H, Tq, T, d, out, lse = _decode_args(q, k, v, k0, v0, out, lse, return_lse, "csa_decode")
     need = csa_decode_workspace_bytes(B, H, Tq, T, d)
     if need < 0:
         raise CsaError(CSA_ERR_INVALID_ARG, "csa_decode (sizes)")
     if workspace is None:
-        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
-    if out is None:
-        out = torch.empty_like(q)
-    else:
-        _check("out", out, (B, H, Tq, d), dt, dev)
-    if lse is None and return_lse:
-        lse = torch.empty((B, H, Tq), dtype=torch.float32, device=dev)
-    elif lse is not None:
-        _check("lse", lse, (B, H, Tq), torch.float32, dev)
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     st = load().csa_decode(
         q.data_ptr(), k.data_ptr(), v.data_ptr(),
         k0.data_ptr() if k0 is not None else None, v0.data_ptr() if v0 is not None else None,
         out.data_ptr(), lse.data_ptr() if lse is not None else None,
         workspace.data_ptr(), workspace.numel() * workspace.element_size(),
-        B, H, Tq, T, d, _dtype_code(q), _stream_handle(stream, dev))
+        B, H, Tq, T, d, _dtype_code(q), _stream_handle(stream, q.device))
     if st != CSA_OK:
         raise CsaError(st, "csa_decode")
+    return out, lse
+
+
+def csa_decode_noalloc(q, k, v, k0=None, v0=None, *, out=None, lse=None, return_lse=True, stream=None):
+    """csa_decode with the library's static device scratch as its workspace (the entry point
+    allocates nothing; pass ``out`` and ``lse`` to keep this wrapper from allocating them).
+    Calls on one GPU share that scratch: calls that can overlap must be ordered by the caller.
+    """
+    B, H, Tq, T, d, out, lse = _decode_args(q, k, v, k0, v0, out, lse, return_lse, "csa_decode_noalloc")
+    st = load().csa_decode_noalloc(
+        q.data_ptr(), k.data_ptr(), v.data_ptr(),
+        k0.data_ptr() if k0 is not None else None, v0.data_ptr() if v0 is not None else None,
+        out.data_ptr(), lse.data_ptr() if lse is not None else None,
+        B, H, Tq, T, d, _dtype_code(q), _stream_handle(stream, q.device))
+    if st != CSA_OK:
+        raise CsaError(st, "csa_decode_noalloc")
     return out, lse
 
 

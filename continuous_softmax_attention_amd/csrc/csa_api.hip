@@ -1,6 +1,9 @@
 // C-ABI entry points of libcsa: csa_forward, csa_forward_first_order,
-// csa_forward_half_interval, csa_decode and csa_backward, each with its argument validation.
+// csa_forward_half_interval, csa_decode, csa_decode_noalloc and csa_backward, each with its
+// argument validation.
 #include <hip/hip_runtime.h>
+
+#include <mutex>
 
 #include "attn16.hpp"
 #include "bwd16.hpp"
@@ -118,15 +121,9 @@ extern "C" int csa_decode_check(const void* q, const void* k, const void* v, con
   return csa::validate_decode(q, k, v, k0, v0, out, lse, workspace, workspace_bytes, B, H, Tq, T, d, dtype);
 }
 
-extern "C" int csa_decode(const void* q, const void* k, const void* v, const void* k0, const void* v0,
-                          void* out, float* lse, void* workspace, int64_t workspace_bytes, int64_t B,
-                          int64_t H, int64_t Tq, int64_t T, int64_t d, int dtype, void* stream) {
-  const int st =
-      csa::validate_decode(q, k, v, k0, v0, out, lse, workspace, workspace_bytes, B, H, Tq, T, d, dtype);
-  if (st != CSA_OK) return st;
-  csa::DecParams p{q, k, v, k0, v0, out, lse, (float*)workspace,
-                   (int)(B * H), (int)Tq, (int)T, 0, 0};  // split plan chosen at launch
-  hipStream_t s = (hipStream_t)stream;
+namespace {
+
+int launch_decode_any(csa::DecParams& p, int64_t d, int dtype, hipStream_t s) {
   hipError_t e = hipErrorInvalidValue;
   if (dtype == CSA_F32) {
     if (d == 16) e = csa::launch_decode<float, 16>(p, s);
@@ -139,6 +136,74 @@ extern "C" int csa_decode(const void* q, const void* k, const void* v, const voi
     else e = csa::launch_decode16<128>(p, s);
   }
   return e == hipSuccess ? CSA_OK : CSA_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" int csa_decode(const void* q, const void* k, const void* v, const void* k0, const void* v0,
+                          void* out, float* lse, void* workspace, int64_t workspace_bytes, int64_t B,
+                          int64_t H, int64_t Tq, int64_t T, int64_t d, int dtype, void* stream) {
+  const int st =
+      csa::validate_decode(q, k, v, k0, v0, out, lse, workspace, workspace_bytes, B, H, Tq, T, d, dtype);
+  if (st != CSA_OK) return st;
+  csa::DecParams p{q, k, v, k0, v0, out, lse, (float*)workspace,
+                   (int)(B * H), (int)Tq, (int)T, 0, 0};  // split plan chosen at launch
+  return launch_decode_any(p, d, dtype, (hipStream_t)stream);
+}
+
+// ---- csa_decode_noalloc: the decode workspace in a static device array.  In host code the
+// array's name stands for a host-side shadow, not for device memory: its device address (one
+// per GPU) is looked up once per device with hipGetSymbolAddress and only that address is
+// handed to kernels.
+static __device__ __align__(256) char scratch[CSA_DECODE_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_dev[kMaxDevices] = {};  // device address of `scratch` on each device, once looked up
+
+// Device address of the scratch on the current device (looked up on the first call there).
+int scratch_on_current_device(void** out, hipStream_t stream) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return CSA_ERR_HIP;
+  if (stream != nullptr) {
+    hipDevice_t sdev = -1;
+    if (hipStreamGetDevice(stream, &sdev) != hipSuccess || sdev != dev) return CSA_ERR_HIP;
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_dev[dev] == nullptr) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || ptr == nullptr) {
+      (void)hipGetLastError();  // the failure is reported by the return code
+      return CSA_ERR_HIP;
+    }
+    g_scratch_dev[dev] = ptr;
+  }
+  *out = g_scratch_dev[dev];
+  return CSA_OK;
+}
+
+}  // namespace
+
+extern "C" int csa_decode_noalloc_check(const void* q, const void* k, const void* v, const void* k0,
+                                        const void* v0, const void* out, const float* lse, int64_t B, int64_t H,
+                                        int64_t Tq, int64_t T, int64_t d, int dtype) {
+  return csa::validate_decode_noalloc(q, k, v, k0, v0, out, lse, CSA_DECODE_NOALLOC_SCRATCH_BYTES, B, H, Tq, T, d,
+                                      dtype);
+}
+
+extern "C" int csa_decode_noalloc(const void* q, const void* k, const void* v, const void* k0, const void* v0,
+                                  void* out, float* lse, int64_t B, int64_t H, int64_t Tq, int64_t T, int64_t d,
+                                  int dtype, void* stream) {
+  int st = csa::validate_decode_noalloc(q, k, v, k0, v0, out, lse, CSA_DECODE_NOALLOC_SCRATCH_BYTES, B, H, Tq, T,
+                                        d, dtype);
+  if (st != CSA_OK) return st;
+  void* ws = nullptr;
+  st = scratch_on_current_device(&ws, (hipStream_t)stream);
+  if (st != CSA_OK) return st;
+  csa::DecParams p{q, k, v, k0, v0, out, lse, (float*)ws, (int)(B * H), (int)Tq, (int)T, 0, 0};
+  return launch_decode_any(p, d, dtype, (hipStream_t)stream);
 }
 
 extern "C" int64_t csa_backward_workspace_bytes(int64_t B, int64_t H, int64_t T, int64_t d) {

@@ -72,6 +72,29 @@ inline int64_t decode_workspace_bytes(int64_t B, int64_t H, int64_t Tq, int64_t 
   return B * H * nsplit * Tq * (d + 2) * 4;
 }
 
+// Everything validate_decode checks except the workspace; with ws == nullptr the workspace
+// is one the library holds (csa_decode_noalloc), which no caller buffer can overlap.
+inline int validate_decode_core(const void* q, const void* k, const void* v, const void* k0, const void* v0,
+                                const void* out, const float* lse, const void* ws, int64_t ws_need, int64_t B,
+                                int64_t H, int64_t Tq, int64_t T, int64_t d, int dtype) {
+  const int64_t esize = dtype == CSA_F32 ? 4 : 2;
+  if (B * H > INT64_MAX / (T * d * esize)) return CSA_ERR_INVALID_ARG;
+  for (const void* p : {q, k, v, out})
+    if (!aligned(p, 16)) return CSA_ERR_INVALID_ARG;
+  if (ws && !aligned(ws, 16)) return CSA_ERR_INVALID_ARG;
+  if (k0 && !aligned(k0, 16)) return CSA_ERR_INVALID_ARG;
+  if (v0 && !aligned(v0, 16)) return CSA_ERR_INVALID_ARG;
+  if (lse && !aligned(lse, 4)) return CSA_ERR_INVALID_ARG;
+  const int64_t cache = B * H * T * d * esize, qbytes = B * H * Tq * d * esize;
+  const Span so = span_of(out, qbytes), sl = span_of(lse, B * H * Tq * 4), sw = span_of(ws, ws_need);
+  const Span ins[5] = {span_of(q, qbytes), span_of(k, cache), span_of(v, cache),
+                       span_of(k0, B * H * d * esize), span_of(v0, B * H * d * esize)};
+  for (const Span& s : ins)
+    if (overlaps(so, s) || overlaps(sl, s) || overlaps(sw, s)) return CSA_ERR_INVALID_ARG;
+  if (overlaps(so, sl) || overlaps(so, sw) || overlaps(sl, sw)) return CSA_ERR_INVALID_ARG;
+  return CSA_OK;
+}
+
 inline int validate_decode(const void* q, const void* k, const void* v, const void* k0, const void* v0,
                            const void* out, const float* lse, const void* ws, int64_t ws_bytes, int64_t B,
                            int64_t H, int64_t Tq, int64_t T, int64_t d, int dtype) {
@@ -80,21 +103,21 @@ inline int validate_decode(const void* q, const void* k, const void* v, const vo
   if (!q || !k || !v || !out || !ws) return CSA_ERR_INVALID_ARG;
   const int64_t need = decode_workspace_bytes(B, H, Tq, T, d);
   if (need < 0 || ws_bytes < need) return CSA_ERR_INVALID_ARG;
-  const int64_t esize = dtype == CSA_F32 ? 4 : 2;
-  if (B * H > INT64_MAX / (T * d * esize)) return CSA_ERR_INVALID_ARG;
-  for (const void* p : {q, k, v, out, ws})
-    if (!aligned(p, 16)) return CSA_ERR_INVALID_ARG;
-  if (k0 && !aligned(k0, 16)) return CSA_ERR_INVALID_ARG;
-  if (v0 && !aligned(v0, 16)) return CSA_ERR_INVALID_ARG;
-  if (lse && !aligned(lse, 4)) return CSA_ERR_INVALID_ARG;
-  const int64_t cache = B * H * T * d * esize, qbytes = B * H * Tq * d * esize;
-  const Span so = span_of(out, qbytes), sl = span_of(lse, B * H * Tq * 4), sw = span_of(ws, need);
-  const Span ins[5] = {span_of(q, qbytes), span_of(k, cache), span_of(v, cache),
-                       span_of(k0, B * H * d * esize), span_of(v0, B * H * d * esize)};
-  for (const Span& s : ins)
-    if (overlaps(so, s) || overlaps(sl, s) || overlaps(sw, s)) return CSA_ERR_INVALID_ARG;
-  if (overlaps(so, sl) || overlaps(so, sw) || overlaps(sl, sw)) return CSA_ERR_INVALID_ARG;
-  return CSA_OK;
+  return validate_decode_core(q, k, v, k0, v0, out, lse, ws, need, B, H, Tq, T, d, dtype);
+}
+
+// csa_decode_noalloc: csa_decode's checks with the library's static scratch of `scratch_bytes`
+// as the workspace; sizes whose workspace exceeds it return CSA_ERR_SCRATCH_TOO_SMALL.
+inline int validate_decode_noalloc(const void* q, const void* k, const void* v, const void* k0, const void* v0,
+                                   const void* out, const float* lse, int64_t scratch_bytes, int64_t B, int64_t H,
+                                   int64_t Tq, int64_t T, int64_t d, int dtype) {
+  if (dtype != CSA_F32 && dtype != CSA_BF16) return CSA_ERR_UNSUPPORTED;
+  if (d != 16 && d != 64 && d != 128) return CSA_ERR_UNSUPPORTED;
+  if (!q || !k || !v || !out) return CSA_ERR_INVALID_ARG;
+  const int64_t need = decode_workspace_bytes(B, H, Tq, T, d);
+  if (need < 0) return CSA_ERR_INVALID_ARG;
+  if (need > scratch_bytes) return CSA_ERR_SCRATCH_TOO_SMALL;
+  return validate_decode_core(q, k, v, k0, v0, out, lse, nullptr, 0, B, H, Tq, T, d, dtype);
 }
 
 // Checks of the backward entry points: bf16 only, d in {64, 128}; q, k, v, o, dO, dq, dk,
@@ -165,6 +188,9 @@ inline const char* status_string(int s) {
     case CSA_ERR_INVALID_ARG: return "invalid argument (null pointer, size, alignment or overlap)";
     case CSA_ERR_UNSUPPORTED: return "unsupported head dimension or dtype";
     case CSA_ERR_HIP: return "HIP launch failure";
+    case CSA_ERR_SCRATCH_TOO_SMALL:
+      return "sizes need more workspace than the static scratch of csa_decode_noalloc holds "
+             "(csa_decode_workspace_bytes > CSA_DECODE_NOALLOC_SCRATCH_BYTES)";
     default: return "unknown status";
   }
 }

@@ -49,7 +49,8 @@ enum {
   CSA_OK = 0,
   CSA_ERR_INVALID_ARG = 1, /* NULL pointer, non-positive size, misaligned or overlapping buffer, size overflow */
   CSA_ERR_UNSUPPORTED = 2, /* head dimension d not in {16, 64, 128}, or a dtype the entry point does not take */
-  CSA_ERR_HIP = 3          /* the kernel launch was rejected by the HIP runtime */
+  CSA_ERR_HIP = 3,         /* the kernel launch was rejected by the HIP runtime */
+  CSA_ERR_SCRATCH_TOO_SMALL = 4 /* csa_decode_noalloc: the sizes need more than its static scratch */
 };
 
 /*
@@ -167,6 +168,41 @@ int csa_decode_check(const void* q, const void* k, const void* v, const void* k0
 
 /* Workspace bytes csa_decode needs for these sizes, or -1 if the sizes are invalid. */
 int64_t csa_decode_workspace_bytes(int64_t B, int64_t H, int64_t Tq, int64_t T, int64_t d);
+
+/*
+ * Bytes of the static device scratch that csa_decode_noalloc uses as its workspace: 64 MiB,
+ * held on every GPU the library runs on until the process ends.
+ */
+#define CSA_DECODE_NOALLOC_SCRATCH_BYTES (64ll << 20)
+
+/*
+ * csa_decode_noalloc -- csa_decode for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * computation, kernels and split plan, with the per-split partial results kept in a static
+ * device array of CSA_DECODE_NOALLOC_SCRATCH_BYTES that the library holds on each GPU instead
+ * of a caller-provided workspace.  The call allocates nothing (no hipMalloc, hipFree or
+ * allocating library routine); its first call on a device looks up that device's copy of the
+ * array once.
+ *
+ *   Arguments as csa_decode without workspace / workspace_bytes; the kernels run on the
+ *   current device, so `stream` (NULL = the null stream) must belong to it.
+ *
+ * Returns CSA_OK; CSA_ERR_SCRATCH_TOO_SMALL (nothing launched) when
+ * csa_decode_workspace_bytes(B, H, Tq, T, d) > CSA_DECODE_NOALLOC_SCRATCH_BYTES; CSA_ERR_HIP
+ * when the scratch cannot be looked up, the stream belongs to another device, or a launch
+ * fails; otherwise the codes of csa_decode.  Every call on one GPU shares that GPU's scratch:
+ * calls that can overlap (different streams, or several host threads) race and must be
+ * ordered by the caller.  The scratch needs no initialisation and keeps the last call's
+ * partial results.
+ */
+int csa_decode_noalloc(const void* q, const void* k, const void* v, const void* k0, const void* v0,
+                       void* out, float* lse, int64_t B, int64_t H, int64_t Tq, int64_t T, int64_t d,
+                       int dtype, void* stream);
+
+/* The argument validation of csa_decode_noalloc alone (no HIP call). */
+int csa_decode_noalloc_check(const void* q, const void* k, const void* v, const void* k0, const void* v0,
+                             const void* out, const float* lse, int64_t B, int64_t H, int64_t Tq, int64_t T,
+                             int64_t d, int dtype);
 
 /*
  * csa_backward -- gradients of the causal forward (eq. (10)-(11)) for training, the use the

@@ -37,6 +37,7 @@ def test_header_declares_the_entry_points():
     assert {"csa_forward", "csa_forward_check", "csa_forward_first_order", "csa_forward_first_order_check",
             "csa_forward_half_interval", "csa_forward_half_interval_check",
             "csa_decode", "csa_decode_check", "csa_decode_workspace_bytes",
+            "csa_decode_noalloc", "csa_decode_noalloc_check",
             "csa_backward", "csa_backward_check", "csa_backward_workspace_bytes",
             "csa_status_string"} <= set(csa.header_functions("csa.h"))
     assert {"std_fwd", "std_fwd_check", "csa_probe"} <= set(csa.header_functions("csa_bench.h"))
@@ -225,6 +226,43 @@ def test_decode_check_rules():
                               a["B"], a["H"], 9, a["T"], a["d"], a["dtype"]) == INV
 
 
+def _ncheck(**kw):
+    a = _dargs(**kw)
+    return csa.csa_decode_noalloc_check(a["q"], a["k"], a["v"], a["k0"], a["v0"], a["out"], a["lse"],
+                                        a["B"], a["H"], a["Tq"], a["T"], a["d"], a["dtype"])
+
+
+def test_decode_noalloc_check_rules():
+    # csa_decode's rules without the workspace arguments, and a size limit: the workspace
+    # csa_decode would need must fit the static scratch
+    cap = csa.CSA_DECODE_NOALLOC_SCRATCH_BYTES
+    assert cap == 64 << 20
+    assert _ncheck() == OK
+    assert _ncheck(k0=A + 300 * MB, v0=A + 301 * MB, lse=None) == OK
+    for d in (16, 64, 128):
+        for dt in (csa.CSA_F32, csa.CSA_BF16):
+            assert _ncheck(d=d, dtype=dt) == OK
+    assert _ncheck(d=96) == UNS
+    for bad in (dict(Tq=0), dict(Tq=9), dict(q=None), dict(out=A + 192 * MB + 2), dict(lse=A + 192 * MB + 16)):
+        assert _ncheck(**bad) == INV, bad
+    # the largest T that fits, and one past it (B16 H8 Tq8 d128: 128 heads x 130 floats x 8 queries)
+    rec = 16 * 8 * 8 * 130 * 4
+    t_fit = (cap // rec) * 64 - 1
+    assert csa.csa_decode_workspace_bytes(16, 8, 8, t_fit, 128) <= cap
+    assert csa.csa_decode_workspace_bytes(16, 8, 8, t_fit + 1, 128) > cap
+    big = dict(B=16, H=8, Tq=8, d=128, k=A + 1024 * MB, v=A + 2048 * MB, out=A + 4096 * MB, lse=A + 4097 * MB)
+    assert _ncheck(T=t_fit, **big) == OK
+    assert _ncheck(T=t_fit + 1, **big) == csa.CSA_ERR_SCRATCH_TOO_SMALL
+    assert "scratch" in csa.status_string(csa.CSA_ERR_SCRATCH_TOO_SMALL)
+    # the launching entry point returns the same codes before any HIP call
+    a = _dargs(T=t_fit + 1, **big)
+    assert csa.csa_decode_noalloc_raw(a["q"], a["k"], a["v"], None, None, a["out"], None, a["B"], a["H"], a["Tq"],
+                                      a["T"], a["d"], a["dtype"]) == csa.CSA_ERR_SCRATCH_TOO_SMALL
+    a = _dargs(Tq=9)
+    assert csa.csa_decode_noalloc_raw(a["q"], a["k"], a["v"], None, None, a["out"], None, a["B"], a["H"], 9,
+                                      a["T"], a["d"], a["dtype"]) == INV
+
+
 def _bargs(**kw):
     big = 2 * 3 * 100 * 64 * 2  # B*H*T*d bf16 bytes of the default sizes (< 1 MB)
     a = dict(q=A, k=A + 1 * MB, v=A + 2 * MB, k0=None, v0=None, o=A + 3 * MB, lse=A + 4 * MB, dout=A + 5 * MB,
@@ -305,7 +343,7 @@ def test_backward_check_rules():
 
 
 def test_status_strings():
-    for s in (OK, INV, UNS, csa.CSA_ERR_HIP, 99):
+    for s in (OK, INV, UNS, csa.CSA_ERR_HIP, csa.CSA_ERR_SCRATCH_TOO_SMALL, 99):
         assert isinstance(csa.status_string(s), str) and csa.status_string(s)
 
 

@@ -25,6 +25,7 @@ from ._lib import (  # noqa: F401
     csa_backward_raw,
     csa_backward_workspace_bytes,
     csa_backward_workspace_bytes_fast,
+    csa_backward_workspace_bytes_kept,
     csa_decode,
     csa_decode_check,
     csa_decode_noalloc,

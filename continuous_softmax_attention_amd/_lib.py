@@ -52,6 +52,7 @@ _SIGS = {
     "csa_backward_check": (ctypes.c_int, [_vp] * 14 + [_i64] * 5 + [ctypes.c_int]),
     "csa_backward_workspace_bytes": (_i64, [_i64] * 4),
     "csa_backward_workspace_bytes_fast": (_i64, [_i64] * 4),
+    "csa_backward_workspace_bytes_kept": (_i64, [_i64] * 5),
     "csa_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "std_fwd": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, ctypes.c_int, _vp]),
     "std_fwd_check": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, ctypes.c_int]),
@@ -155,6 +156,15 @@ def csa_backward_check(q, k, v, k0, v0, o, lse, dout, dq, dk, dv, dk0, dv0, ws, 
 def csa_backward_workspace_bytes(B, H, T, d) -> int:
     """Bytes of workspace csa_backward needs (-1 for invalid sizes)."""
     return int(load().csa_backward_workspace_bytes(B, H, T, d))
+
+
+def csa_backward_workspace_bytes_kept(B, H, T, d, heads_per_group) -> int:
+    """Bytes with which csa_backward keeps dS for heads_per_group heads at a time (-1: invalid)."""
+    return int(load().csa_backward_workspace_bytes_kept(B, H, T, d, heads_per_group))
+
+
+# default budget of the kept-dS workspace the binding allocates (dS grows as T^2 per head)
+KEPT_DS_BUDGET_BYTES = 2 << 30
 
 
 def csa_backward_workspace_bytes_fast(B, H, T, d) -> int:
@@ -401,11 +411,17 @@ def csa_backward(q, k, v, o, lse, dout, k0=None, v0=None, *, sink_grads=True, dq
     if need < 0:
         raise CsaError(CSA_ERR_UNSUPPORTED if d not in (64, 128) else CSA_ERR_INVALID_ARG, "csa_backward (sizes)")
     if workspace is None:
-        # the kept-dS workspace grows as T^2: take it only while it is a modest share of the
-        # free device memory, else the O(B H T) workspace (dS recomputed; identical results)
-        fast = csa_backward_workspace_bytes_fast(B, H, T, d)
+        # dS kept for as many heads at a time as fit min(2 GiB, a quarter of the free device
+        # memory) -- it grows as T^2 per head -- else the O(B H T) workspace (dS recomputed);
+        # the results are identical either way
         free, _ = torch.cuda.mem_get_info(dev)
-        size = fast if 0 < fast <= free // 4 else need
+        budget = min(KEPT_DS_BUDGET_BYTES, free // 4)
+        one = csa_backward_workspace_bytes_kept(B, H, T, d, 1)
+        size = need
+        if 0 < one <= budget:
+            per_head = csa_backward_workspace_bytes_kept(B, H, T, d, 2) - one if B * H > 1 else 0
+            heads = B * H if per_head == 0 else min(B * H, 1 + (budget - one) // per_head)
+            size = csa_backward_workspace_bytes_kept(B, H, T, d, heads)
         workspace = torch.empty(size, dtype=torch.uint8, device=dev)
     grads = []
     for name, t in (("dq", dq), ("dk", dk), ("dv", dv)):

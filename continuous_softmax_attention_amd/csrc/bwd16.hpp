@@ -67,6 +67,8 @@ struct BwdParams {
   int B, H, T;
   char* ds;          // dS tiles (optional last workspace region), or null: dq recomputes dS
   int64_t ds_tiles;  // dS tiles per (b, h)
+  int h0, nh;        // heads h0 .. h0 + nh - 1 (of the B*H) in this launch; the dS region holds
+                     // the tiles of these nh heads (the launch's head index 0 .. nh - 1)
 };
 
 // dS tiles for the dq product: for every (b, h), query block qb (128 rows) and key tile
@@ -179,13 +181,17 @@ __device__ __forceinline__ void lds_copy16_ptr(const char* src, unsigned lds_add
 #pragma clang diagnostic pop
 
 // ---------------------------------------------------------------- per-element arithmetic
-// Edge (i, i+1) of one query from alpha_i, p_i, alpha_{i+1}, p_{i+1}: R/Z, L/Z and c_e as in
-// the header; all three zero when the edge does not exist (selects, so that values of
-// positions that do not exist for this query never reach the result).  MASKED = false: the
-// caller knows that every edge exists and the selects are left out.
+// Edge (i, i+1) of one query from alpha_i, p_i, alpha_{i+1}, p_{i+1}: W = Lprev + R/Z (the
+// finished P of position i when Lprev is its left term), L/Z and c_e as in the header.  When
+// the edge does not exist, W = Lprev and L = c_e = 0 (selects, so that values of positions
+// that do not exist for this query never reach the result).  MASKED = false: the caller knows
+// that every edge exists and the selects are left out.  Every operation is written out
+// (contraction off): an existing edge gets the same bits in both forms, so the kernels that
+// compute dS (bwd_dq, bwd_dkdv) agree bit for bit whichever form each takes for a tile.
 template <bool MASKED>
-__device__ __forceinline__ void edge_grad(float al, float pl, float ar, float pr, bool exists, float& R,
-                                          float& L, float& C) {
+__device__ __forceinline__ void edge_grad(float al, float pl, float ar, float pr, bool exists, float Lprev,
+                                          float& W, float& L, float& C) {
+#pragma clang fp contract(off)
   constexpr float k0 = 0.2402265069591007f;     // c^2/2
   constexpr float k1 = 0.055504108664821576f;   // c^3/6
   constexpr float m0 = 0.08007550231970023f;    // c^2/6
@@ -193,26 +199,27 @@ __device__ __forceinline__ void edge_grad(float al, float pl, float ar, float pr
   constexpr float m2 = 0.005770877464577086f;   // c^4/40
   constexpr float two_over_c = 2.8853900817779268f;
   const float y = ar - al;
+  const float ay = __builtin_fabsf(y);
+  const bool small = ay < 0.07f;
   const float u = __builtin_amdgcn_rcpf(y);
   const float du = (pr - pl) * u;
-  float r = __builtin_fmaf(-kLn2, pl, du) * u;
-  float l = __builtin_fmaf(kLn2, pr, -du) * u;
-  float c = __builtin_fmaf(-two_over_c, du, pl + pr) * (u * u);
-  const float ay = __builtin_fabsf(y);
-  const float rt = pl * __builtin_fmaf(y, k1, k0);
+  const float w = __builtin_fmaf(__builtin_fmaf(-kLn2, pl, du), u, Lprev);
+  const float l = __builtin_fmaf(kLn2, pr, -du) * u;
+  const float c = __builtin_fmaf(-two_over_c, du, pl + pr) * (u * u);
+  const float wt = __builtin_fmaf(pl, __builtin_fmaf(y, k1, k0), Lprev);
   const float lt = pr * __builtin_fmaf(y, -k1, k0);
   const float ct = pl * __builtin_fmaf(y, __builtin_fmaf(y, m2, m1), m0);
-  r = ay < 0.07f ? rt : r;
-  l = ay < 0.07f ? lt : l;
-  c = ay < 0.25f ? ct : c;
+  const float wv = small ? wt : w;
+  const float lv = small ? lt : l;
+  const float cv = ay < 0.25f ? ct : c;
   if constexpr (MASKED) {
-    R = exists ? r : 0.0f;
-    L = exists ? l : 0.0f;
-    C = exists ? c : 0.0f;
+    W = exists ? wv : Lprev;
+    L = exists ? lv : 0.0f;
+    C = exists ? cv : 0.0f;
   } else {
-    R = r;
-    L = l;
-    C = c;
+    W = wv;
+    L = lv;
+    C = cv;
   }
 }
 
@@ -225,14 +232,15 @@ template <bool MASKED>
 __device__ __forceinline__ void tile_grad(const float (&s)[16], const float (&dp)[16], float sl, float dpl,
                                           float sr, float dpr, float mu, float delta, int lim, float (&P)[16],
                                           float (&dS)[16], float& p_left, float& ds_left) {
+#pragma clang fp contract(off)
   auto alpha = [&](float x) { return __builtin_fmaf(x, kLog2e, -mu); };
   float aC = alpha(sl), pC = exp2_fast(aC), dC = dpl;
   float aN = alpha(s[0]), pN = exp2_fast(aN), dN = dp[0];
-  float R, L, C;
-  edge_grad<MASKED>(aC, pC, aN, pN, 0 <= lim, R, L, C);
+  float W, L, C;
+  edge_grad<MASKED>(aC, pC, aN, pN, 0 <= lim, 0.0f, W, L, C);
   float G = C * (dC - dN);
-  p_left = R;
-  ds_left = __builtin_fmaf(R, dC - delta, -G);
+  p_left = W;
+  ds_left = __builtin_fmaf(W, dC - delta, -G);
   float Lprev = L, Gprev = G;
   aC = aN;
   pC = pN;
@@ -247,11 +255,10 @@ __device__ __forceinline__ void tile_grad(const float (&s)[16], const float (&dp
       dN = dpr;
     }
     pN = exp2_fast(aN);
-    edge_grad<MASKED>(aC, pC, aN, pN, t + 1 <= lim, R, L, C);
+    edge_grad<MASKED>(aC, pC, aN, pN, t + 1 <= lim, Lprev, W, L, C);
     G = C * (dC - dN);
-    const float pt = Lprev + R;
-    P[t] = pt;
-    dS[t] = __builtin_fmaf(pt, dC - delta, Gprev - G);
+    P[t] = W;
+    dS[t] = __builtin_fmaf(W, dC - delta, Gprev - G);
     Lprev = L;
     Gprev = G;
     aC = aN;
@@ -417,9 +424,10 @@ __global__ void __launch_bounds__(512, 2) bwd_dq_kernel(BwdParams p) {
   const int n = lane & 15, g = lane >> 4;
   const int Tn = p.T, BH = p.B * p.H;
   const int nqb = (Tn + kBlockRows - 1) / kBlockRows;
-  int bh, qrank;
-  xcd_head_order<4>(blockIdx.x, BH, nqb, bh, qrank);  // as the forward
-  const int qb = nqb - 1 - qrank;                     // longest query blocks first
+  int bhl, qrank;
+  xcd_head_order<4>(blockIdx.x, p.nh, nqb, bhl, qrank);  // as the forward, over the launch's heads
+  const int bh = p.h0 + bhl;
+  const int qb = nqb - 1 - qrank;                        // longest query blocks first
   const int q0 = qb * kBlockRows;
   const int qw = q0 + 16 * wave;
   const int qr = qw + n;
@@ -561,9 +569,10 @@ __global__ void __launch_bounds__(512, 2) bwd_dq_from_ds_kernel(BwdParams p) {
   const int n = lane & 15, g = lane >> 4;
   const int Tn = p.T, BH = p.B * p.H;
   const int nqb = (Tn + kBlockRows - 1) / kBlockRows;
-  int bh, qrank;
-  xcd_head_order<4>(blockIdx.x, BH, nqb, bh, qrank);  // as the forward
-  const int qb = nqb - 1 - qrank;                     // longest query blocks first
+  int bhl, qrank;
+  xcd_head_order<4>(blockIdx.x, p.nh, nqb, bhl, qrank);  // as the forward, over the launch's heads
+  const int bh = p.h0 + bhl;
+  const int qb = nqb - 1 - qrank;                        // longest query blocks first
   const int q0 = qb * kBlockRows;
   const int qw = q0 + 16 * wave;
   const int qr = qw + n;
@@ -574,7 +583,7 @@ __global__ void __launch_bounds__(512, 2) bwd_dq_from_ds_kernel(BwdParams p) {
 
   const size_t head = (size_t)bh * (size_t)Tn * D;
   const char* Kg = (const char*)((const bf16*)p.k + head);
-  const char* dsl = p.ds + ((size_t)bh * (size_t)p.ds_tiles + (size_t)ds_tile_index(qb, 0)) * kDsTileBytes +
+  const char* dsl = p.ds + ((size_t)bhl * (size_t)p.ds_tiles + (size_t)ds_tile_index(qb, 0)) * kDsTileBytes +
                     (size_t)(wave * 64 + lane) * 32;
   const int toff = tr_layout_src<ROWB>(tid);
   int vbase[2];
@@ -717,8 +726,9 @@ __global__ void __launch_bounds__(512, 2) bwd_dkdv_kernel(BwdParams p) {
   // heads four at a time per XCD, key block 0 (the most queries) first: against heads-fastest
   // order, fetched bytes per lm launch 1285 -> 458 MB with two heads at a time and 1.3% faster;
   // four at a time is 1.4% faster again (one at a time: 1% slower than two)
-  int bh, kb;
-  xcd_head_order<4>(blockIdx.x, BH, (Tn + kTile - 1) / kTile, bh, kb);
+  int bhl, kb;
+  xcd_head_order<4>(blockIdx.x, p.nh, (Tn + kTile - 1) / kTile, bhl, kb);
+  const int bh = p.h0 + bhl;
   const int J = kb * kTile;
   const BwdWs ws = bwd_ws(p.ws, BH, Tn);
 
@@ -812,7 +822,7 @@ __global__ void __launch_bounds__(512, 2) bwd_dkdv_kernel(BwdParams p) {
     // keys 16g + 8h + e = chunks 2g + h of the P / dS row
     char* dst = nullptr;
     if constexpr (WRITE_DS) {
-      dst = p.ds + ((size_t)bh * (size_t)p.ds_tiles + (size_t)ds_tile_index(it, kb)) * kDsTileBytes +
+      dst = p.ds + ((size_t)bhl * (size_t)p.ds_tiles + (size_t)ds_tile_index(it, kb)) * kDsTileBytes +
             (size_t)(wave * 64 + lane) * 32;
       if (J == 0 && g == 0 && qr < Tn) {
         ws.p0[(size_t)bh * Tn + qr] = pl;
@@ -878,11 +888,18 @@ __global__ void __launch_bounds__(512, 2) bwd_dkdv_kernel(BwdParams p) {
   }
 }
 
+// prm.h0 = 0 and prm.nh = B*H on entry.  With dS kept (prm.ds set), prm.nh is the number of
+// heads whose dS tiles fit the workspace: bwd_dkdv and bwd_dq_from_ds run on groups of that
+// many heads in turn (the second reads the tiles the first wrote for the same group).
 template <int D>
-inline hipError_t launch_backward(const BwdParams& prm, hipStream_t stream) {
-  const int64_t BH = (int64_t)prm.B * prm.H;
-  const int64_t rows = BH * prm.T;
+inline hipError_t launch_backward(const BwdParams& prm_in, hipStream_t stream) {
+  BwdParams prm = prm_in;
+  const int BH = prm.B * prm.H;
+  const int64_t rows = (int64_t)BH * prm.T;
   const int rpb = 4 * (64 / (D / 8));  // rows per pre block
+  const int group = prm.nh;
+  prm.h0 = 0;
+  prm.nh = BH;
   hipLaunchKernelGGL((bwd_pre_kernel<D>), dim3((unsigned)((rows + rpb - 1) / rpb)), dim3(256), 0, stream, prm);
   const int nqb = (prm.T + kBlockRows - 1) / kBlockRows;
   const int nkb = (prm.T + kTile - 1) / kTile;
@@ -893,9 +910,14 @@ inline hipError_t launch_backward(const BwdParams& prm, hipStream_t stream) {
     }
   };
   if (prm.ds != nullptr) {  // dS computed once (in bwd_dkdv) and stored; dq is then a plain product
-    hipLaunchKernelGGL((bwd_dkdv_kernel<D, true>), dim3((unsigned)(nkb * BH)), dim3(512), 0, stream, prm);
-    sink();
-    hipLaunchKernelGGL((bwd_dq_from_ds_kernel<D>), dim3((unsigned)(nqb * BH)), dim3(512), 0, stream, prm);
+    for (int h0 = 0; h0 < BH; h0 += group) {
+      BwdParams g = prm;
+      g.h0 = h0;
+      g.nh = BH - h0 < group ? BH - h0 : group;
+      hipLaunchKernelGGL((bwd_dkdv_kernel<D, true>), dim3((unsigned)(nkb * g.nh)), dim3(512), 0, stream, g);
+      hipLaunchKernelGGL((bwd_dq_from_ds_kernel<D>), dim3((unsigned)(nqb * g.nh)), dim3(512), 0, stream, g);
+    }
+    sink();  // reads P and dS of position 0, written by bwd_dkdv for every head
   } else {  // dS recomputed by bwd_dq (workspace without the dS tiles)
     hipLaunchKernelGGL((bwd_dq_kernel<D>), dim3((unsigned)(nqb * BH)), dim3(512), 0, stream, prm);
     sink();

@@ -214,6 +214,11 @@ extern "C" int64_t csa_backward_workspace_bytes_fast(int64_t B, int64_t H, int64
   return csa::backward_workspace_bytes_fast(B, H, T, d);
 }
 
+extern "C" int64_t csa_backward_workspace_bytes_kept(int64_t B, int64_t H, int64_t T, int64_t d,
+                                                     int64_t heads_per_group) {
+  return csa::backward_workspace_bytes_kept(B, H, T, d, heads_per_group);
+}
+
 extern "C" int csa_backward_check(const void* q, const void* k, const void* v, const void* k0, const void* v0,
                                   const void* o, const float* lse, const void* dout, const void* dq,
                                   const void* dk, const void* dv, const void* dk0, const void* dv0,
@@ -230,10 +235,12 @@ extern "C" int csa_backward(const void* q, const void* k, const void* v, const v
   const int st = csa::validate_backward(q, k, v, k0, v0, o, lse, dout, dq, dk, dv, dk0, dv0, workspace,
                                         workspace_bytes, B, H, T, d, dtype);
   if (st != CSA_OK) return st;
-  const int64_t fast = csa::backward_workspace_bytes_fast(B, H, T, d);
-  char* ds = fast > 0 && workspace_bytes >= fast ? (char*)workspace + csa::backward_ds_offset(B, H, T, d) : nullptr;
+  // dS kept for as many heads at a time as the workspace holds (the kernels run on groups of
+  // that many heads), else recomputed
+  const int64_t kept = csa::backward_kept_heads(B, H, T, d, workspace_bytes);
+  char* ds = kept > 0 ? (char*)workspace + csa::backward_ds_offset(B, H, T, d) : nullptr;
   csa::BwdParams p{q, k, v, k0, v0, o, lse, dout, dq, dk, dv, dk0, dv0, (char*)workspace,
-                   (int)B, (int)H, (int)T, ds, csa::backward_ds_tiles_per_head(T)};
+                   (int)B, (int)H, (int)T, ds, csa::backward_ds_tiles_per_head(T), 0, (int)kept};
   const hipError_t e = d == 64 ? csa::launch_backward<64>(p, (hipStream_t)stream)
                                : csa::launch_backward<128>(p, (hipStream_t)stream);
   return e == hipSuccess ? CSA_OK : CSA_ERR_HIP;

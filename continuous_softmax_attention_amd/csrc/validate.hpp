@@ -144,12 +144,26 @@ inline int64_t backward_ds_offset(int64_t B, int64_t H, int64_t T, int64_t d) {
   const int64_t base = backward_workspace_bytes(B, H, T, d);
   return base < 0 ? -1 : (base + 255) / 256 * 256;
 }
-inline int64_t backward_workspace_bytes_fast(int64_t B, int64_t H, int64_t T, int64_t d) {
+// Workspace with which the dS tiles of `heads` heads at a time are kept (1 <= heads <= B*H;
+// the kernels then run on groups of that many heads), or -1.
+inline int64_t backward_workspace_bytes_kept(int64_t B, int64_t H, int64_t T, int64_t d, int64_t heads) {
   const int64_t off = backward_ds_offset(B, H, T, d);
-  if (off < 0) return -1;
+  if (off < 0 || heads < 1 || heads > B * H) return -1;
   const int64_t tiles = backward_ds_tiles_per_head(T);
-  if (tiles > (int64_t(1) << 62) / kBwdDsTileBytes / (B * H)) return -1;
-  return off + B * H * tiles * kBwdDsTileBytes;
+  if (tiles > (int64_t(1) << 62) / kBwdDsTileBytes / heads) return -1;
+  return off + heads * tiles * kBwdDsTileBytes;
+}
+inline int64_t backward_workspace_bytes_fast(int64_t B, int64_t H, int64_t T, int64_t d) {
+  if (B < 1 || H < 1) return -1;
+  return backward_workspace_bytes_kept(B, H, T, d, B * H);
+}
+// Heads whose dS tiles fit a workspace of ws_bytes (0: the recompute path), at most B*H.
+inline int64_t backward_kept_heads(int64_t B, int64_t H, int64_t T, int64_t d, int64_t ws_bytes) {
+  const int64_t one = backward_workspace_bytes_kept(B, H, T, d, 1);
+  if (one < 0 || ws_bytes < one) return 0;
+  const int64_t per_head = backward_ds_tiles_per_head(T) * kBwdDsTileBytes;
+  const int64_t g = 1 + (ws_bytes - one) / per_head;
+  return g < B * H ? g : B * H;
 }
 
 inline int validate_backward(const void* q, const void* k, const void* v, const void* k0, const void* v0,
@@ -161,8 +175,8 @@ inline int validate_backward(const void* q, const void* k, const void* v, const 
   if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv || !ws) return CSA_ERR_INVALID_ARG;
   const int64_t need_min = backward_workspace_bytes(B, H, T, d);
   if (need_min < 0 || ws_bytes < need_min) return CSA_ERR_INVALID_ARG;
-  const int64_t need_fast = backward_workspace_bytes_fast(B, H, T, d);
-  const int64_t need = need_fast > 0 && ws_bytes >= need_fast ? need_fast : need_min;  // the part used
+  const int64_t kept = backward_kept_heads(B, H, T, d, ws_bytes);
+  const int64_t need = kept > 0 ? backward_workspace_bytes_kept(B, H, T, d, kept) : need_min;  // the part used
   for (const void* p : {q, k, v, o, dout, dq, dk, dv, ws})
     if (!aligned(p, 16)) return CSA_ERR_INVALID_ARG;
   for (const void* p : {k0, v0, dk0, dv0})

@@ -226,9 +226,12 @@ int csa_decode_noalloc_check(const void* q, const void* k, const void* v, const 
  *              when k0 / v0 is NULL (the gradient at the zero vector).
  *   workspace  device, 16-byte aligned, at least csa_backward_workspace_bytes(B, H, T, d)
  *              bytes, caller-owned scratch (no initialisation needed); calls sharing it must be
- *              ordered on one stream.  With at least csa_backward_workspace_bytes_fast(B, H, T,
- *              d) bytes the call also keeps dS (bf16, about B*H*T*T bytes) so that it is
- *              computed once instead of twice; the results are identical either way.
+ *              ordered on one stream.  With at least csa_backward_workspace_bytes_kept(B, H, T,
+ *              d, 1) bytes the call also keeps dS (bf16, about T*T bytes per head) so that it is
+ *              computed once instead of twice: for as many heads at a time as the workspace
+ *              holds (all B*H with csa_backward_workspace_bytes_fast bytes), the dk/dv and dq
+ *              kernels running on one group of heads after another.  The results are bitwise
+ *              identical whichever path and group size the workspace selects.
  *   d          64 or 128 (16 returns CSA_ERR_UNSUPPORTED); dtype must be CSA_BF16.
  *   stream     hipStream_t or NULL.
  *
@@ -259,6 +262,13 @@ int64_t csa_backward_workspace_bytes(int64_t B, int64_t H, int64_t T, int64_t d)
  * fit in an int64.
  */
 int64_t csa_backward_workspace_bytes_fast(int64_t B, int64_t H, int64_t T, int64_t d);
+
+/*
+ * Workspace bytes with which csa_backward keeps dS for `heads_per_group` heads at a time
+ * (1 <= heads_per_group <= B*H; B*H gives csa_backward_workspace_bytes_fast): the bounded
+ * form of the faster path for long sequences.  -1 if the sizes are invalid.
+ */
+int64_t csa_backward_workspace_bytes_kept(int64_t B, int64_t H, int64_t T, int64_t d, int64_t heads_per_group);
 
 /* Static, NUL-terminated description of a return code. */
 const char* csa_status_string(int status);

@@ -20,7 +20,7 @@ import pytest
 import torch
 
 import continuous_softmax_attention_amd as csa
-from oracle import csa_backward_reference
+from oracle import csa_backward_reference, csa_backward_row
 from workloads import make_grad_output, make_inputs
 
 pytestmark = pytest.mark.gpu
@@ -149,12 +149,12 @@ def test_workspace_reuse_with_smaller_second_call():
 @pytest.mark.parametrize("T", [1, 2, 63, 64, 65, 127, 128, 129, 200, 300, 1000])
 def test_kept_ds_and_recomputed_ds_paths_agree(T, d):
     # with csa_backward_workspace_bytes_fast bytes dS is computed once (bwd_dkdv) and kept
-    # for dq; with the minimum it is recomputed (bwd_dq).  Same products in the same order,
-    # but a tile may take the compiled form with or without the existence selects in one
-    # kernel and the other form in the other, and the compiler fuses a multiply and an add
-    # into one fma in one form only: dS can differ in its last bf16 bit.  The paths must
-    # agree to a quarter of the parity bar (and each is checked against the reference by
-    # the other tests: the binding's default workspace takes the kept-dS path).
+    # for dq; with the minimum it is recomputed (bwd_dq).  Both kernels form P and dS with the
+    # same written-out operations (no contraction left to the compiler, and the same values for
+    # an existing edge whether a tile takes the masked form or not) and dq with the same
+    # products in the same order, so the two paths must give identical bits.  (Each path is
+    # also checked against the reference by the other tests: the binding's default workspace
+    # takes the kept-dS path.)
     q, k, v, k0, v0, do = _random_case(2, 2, T, d, seed=3000 + T + d)
     qg, kg, vg, k0g, v0g, dog = _gpu(q, k, v, k0, v0, do)
     o, lse = csa.csa_forward(qg, kg, vg, k0g, v0g)
@@ -164,7 +164,66 @@ def test_kept_ds_and_recomputed_ds_paths_agree(T, d):
     b = [_np(g) for g in csa.csa_backward(qg, kg, vg, o, lse, dog, k0g, v0g, workspace=hi)]
     torch.cuda.synchronize()
     for name, x, y in zip(NAMES, a, b):
-        assert np.abs(x - y).max() <= 0.25 * TOL * max(1.0, float(np.abs(y).max())), name
+        assert np.array_equal(x, y), (name, float(np.abs(x - y).max()))
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_kept_ds_in_head_groups_identical(d):
+    # a workspace that holds the dS tiles of 1, 2 or 4 of the 6 heads: the dk/dv and dq kernels
+    # run on groups of that many heads in turn; every group size gives the bits of the
+    # all-heads workspace and of the recompute path
+    B, H, T = 2, 3, 300
+    q, k, v, k0, v0, do = _random_case(B, H, T, d, seed=4100 + d)
+    qg, kg, vg, k0g, v0g, dog = _gpu(q, k, v, k0, v0, do)
+    o, lse = csa.csa_forward(qg, kg, vg, k0g, v0g)
+    sizes = [csa.csa_backward_workspace_bytes(B, H, T, d)]
+    sizes += [csa.csa_backward_workspace_bytes_kept(B, H, T, d, g) for g in (1, 2, 4, 6)]
+    assert sizes[-1] == csa.csa_backward_workspace_bytes_fast(B, H, T, d)
+    assert sizes[1] + 1 < sizes[2]
+    outs = []
+    for nb in sizes + [sizes[2] - 1]:  # the last: one byte short of two heads (one head per group)
+        ws = torch.empty(nb, dtype=torch.uint8, device=DEV)
+        outs.append([_np(g) for g in csa.csa_backward(qg, kg, vg, o, lse, dog, k0g, v0g, workspace=ws)])
+    torch.cuda.synchronize()
+    for i, got in enumerate(outs[1:], 1):
+        for name, x, y in zip(NAMES, got, outs[0]):
+            assert np.array_equal(x, y), (i, name)
+    _compare(f"head groups d{d}", outs[0], csa_backward_reference(q, k, v, do, k0, v0))
+
+
+def test_long_workload_full_size():
+    """The long workload (B1 H32 T16384 d128) at full size with the binding's default workspace
+    (dS kept for the heads that fit 2 GiB at a time): every head finite and checked against
+    the shift symmetries; dq on sampled rows and dk, dv of the last 8 positions of two heads
+    against the reference (a position's dk, dv take the queries at and after it only)."""
+    print("[backward] workload long full size", flush=True)
+    q, k, v, k0, v0 = make_inputs("long")
+    do = make_grad_output(q.shape, q.dtype, 4)
+    B, H, T, d = q.shape
+    per_head = csa.csa_backward_workspace_bytes_kept(B, H, T, d, 2) - csa.csa_backward_workspace_bytes_kept(B, H, T, d, 1)
+    print(f"[backward] long: dS per head {per_head / 2**20:.0f} MiB; "
+          f"all heads {csa.csa_backward_workspace_bytes_fast(B, H, T, d) / 2**30:.2f} GiB", flush=True)
+    got = _run(q, k, v, k0, v0, do)
+    _check_shift_symmetries("long", do, got)
+    dq, dk, dv = got[:3]
+    m = 8
+    for h in (0, 31):
+        qh, kh, vh, doh = (x[0, h].double().numpy() for x in (q, k, v, do))
+        k_hat = np.concatenate([np.zeros((1, d)), kh])
+        v_hat = np.concatenate([np.zeros((1, d)), vh])
+        rows = sorted({0, 1, 63, 64, 4095, 8191, 12000, T - m - 1} | set(range(T - m, T)))
+        gk = np.zeros((m, d))
+        gv = np.zeros((m, d))
+        dq_ref = np.zeros((len(rows), d))
+        for j, r in enumerate(rows):
+            gq, gkr, gvr = csa_backward_row(qh[r], k_hat, v_hat, r + 1, doh[r])
+            dq_ref[j] = gq
+            if r >= T - m:  # contributions to positions T-m+1 .. t (of the rows T-m .. T-1)
+                nn = gkr.shape[0] - (T - m + 1)
+                gk[:nn] += gkr[T - m + 1:]
+                gv[:nn] += gvr[T - m + 1:]
+        _compare(f"long head {h} (dq on {len(rows)} rows, dk/dv of the last {m} positions)",
+                 [dq[0, h, rows], dk[0, h, T - m:], dv[0, h, T - m:]], [dq_ref, gk, gv], names=("dq", "dk", "dv"))
 
 
 def test_rejects_unsupported_before_launch():

@@ -66,6 +66,12 @@ def _cpu_task(args):
     return int(np.sum(rows + 1))
 
 
+# Worker processes of the CPU leg: the GPU machine gives one GPU a share of 16 host cores, whatever
+# os.sched_getaffinity shows there (the whole host's cores may be listed), so the pool takes at
+# most 16; the host's own count is reported beside it.
+CPU_WORKERS_MAX = 16
+
+
 def cpu_baseline(w, q, k, v, k0, v0, heads=64, rows_per_head=320, seed=123):
     """Time the float64 reference on a seeded sample of (head, row) pairs.
 
@@ -84,13 +90,15 @@ def cpu_baseline(w, q, k, v, k0, v0, heads=64, rows_per_head=320, seed=123):
         tasks.append((int(bh) // w.H, int(bh) % w.H, rows))
     _CPU.update(q=q.float().numpy(), k=k.float().numpy(), v=v.float().numpy(),
                 k0=None if k0 is None else k0.float().numpy(), v0=None if v0 is None else v0.float().numpy())
-    workers = max(1, min(16, len(os.sched_getaffinity(0))))
+    host_cores = len(os.sched_getaffinity(0))
+    workers = max(1, min(CPU_WORKERS_MAX, host_cores))
     os.environ.setdefault("OMP_NUM_THREADS", "1")
     ctx = mp.get_context("fork")
     t0 = time.perf_counter()
     with ctx.Pool(workers) as pool:
         done = pool.map(_cpu_task, tasks, chunksize=1)
     dt = time.perf_counter() - t0
+    _CPU.clear()
     positions = sum(done)                      # sum over sampled rows of (t + 1)
     flop = 4.0 * w.d * positions               # same convention as the metric
     total_rows = w.B * w.H * w.T
@@ -99,14 +107,22 @@ def cpu_baseline(w, q, k, v, k0, v0, heads=64, rows_per_head=320, seed=123):
         "value": rate / 1e12,
         "unit": "TFLOP/s",
         "cores": workers,
+        "host_cores": host_cores,
         "kind": "oracle",
         "sample": (f"{len(tasks)} of {nheads} heads x {rows_per_head} seeded query rows "
                    f"({len(tasks) * rows_per_head} of {total_rows} rows), float64 eq. (8), "
-                   f"{workers} worker processes, {dt:.1f} s wall"),
+                   f"{workers} worker processes (of {host_cores} cores in the affinity mask; "
+                   f"one GPU's share of the box is {CPU_WORKERS_MAX}), {dt:.1f} s wall"),
         "sample_s": round(dt, 2),
         # the whole workload at the sampled rate (row cost grows with t + 1, counted in the FLOP)
         "extrapolated_full_s": round(float(w.flop) / rate, 1),
+        "extrapolation": "full-workload seconds = metric FLOP / (FLOP of the sampled rows / sample_s); "
+                         "a row's cost grows with t + 1, which the FLOP of a row counts",
     }
+
+
+# the other bf16 configurations, timed after the headline: (workload, oracle heads, rows per head)
+OTHER_CONFIGS = (("long", 32, 40), ("stress", 16, 80))
 
 
 # ------------------------------------------------------------------ HBM traffic
@@ -179,7 +195,8 @@ def time_kernel(fn, steps, warmup, stream, settle_s=None):
 
 
 # iterations per probe launch: ~2-3 ms each at four waves per SIMD
-_PROBE_ITERS = {0: 20000, 1: 40000, 2: 20000, 3: 20000, 4: 10000, 5: 20000, 6: 10000, 7: 10000, 8: 10000}
+_PROBE_ITERS = {0: 20000, 1: 40000, 2: 20000, 3: 20000, 4: 10000, 5: 20000, 6: 10000, 7: 10000, 8: 10000,
+                9: 3000, 10: 30000, 11: 30000, 12: 10000}
 _PROBE_PER_ITER = {0: 4, 1: 8, 2: 8, 3: 8, 5: 2}  # instructions of the kind per iteration
 _PROBE_WAVES = 4096  # four per SIMD of the 256 CUs
 
@@ -329,6 +346,22 @@ def probes_mode():
                                           "weights_mfma32x32x16": w[8]["cycles_per_wave_iteration"]},
             "mfma32_over_mfma16": round(w[8]["ms"] / w[7]["ms"], 3)}
     out["weights_and_mfma"] = tiling
+    # does a transcendental take issue slots of the plain VALU?  8 FMA chains alone (kind 1) and
+    # with 2 exp / rcp chains beside them (kinds 10, 11), cycles per wave-iteration
+    mix = simd_probes([1, 2, 3, 10, 11], stream)
+    c = {k: mix[k]["cycles_per_wave_iteration"] for k in (1, 10, 11)}
+    out["fma_with_transcendentals"] = {
+        "fma8": c[1], "fma8_exp2": c[10], "fma8_rcp2": c[11],
+        "exp2_alone": round(mix[2]["cycles_per_wave_iteration"] / 4, 1),
+        "rcp2_alone": round(mix[3]["cycles_per_wave_iteration"] / 4, 1)}
+    # the weights by three routes, two keys per wave-iteration at 4 waves per SIMD: the p-form of
+    # the kernels (kind 6), the log-domain form of eq. (13) (kind 9), and the p-form with the
+    # reciprocal replaced by an LDS table (kind 12)
+    wr = simd_probes([6, 9, 12], stream)
+    cw = {k: wr[k]["cycles_per_wave_iteration"] for k in (6, 9, 12)}
+    out["weight_routes"] = {"cycles_per_wave_iteration": {"p_form": cw[6], "log_domain": cw[9], "lds_table": cw[12]},
+                            "log_domain_over_p_form": round(cw[9] / cw[6], 3),
+                            "lds_table_over_p_form": round(cw[12] / cw[6], 3)}
     print(json.dumps(out), flush=True)
 
 
@@ -347,6 +380,8 @@ def main():
     ap.add_argument("--no-half-interval", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-backward", action="store_true")
+    ap.add_argument("--no-other-configs", action="store_true",
+                    help="skip the long and stress configurations (extra keys of the JSON line)")
     ap.add_argument("--probes", action="store_true",
                     help="print the SIMD micro-benchmarks (MFMA-only ceiling, VALU / exp / rcp issue cost, "
                          "MFMA and VALU in one wave) as one JSON line and exit")
@@ -374,6 +409,13 @@ def main():
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(w, q, k, v, k0, v0)
+    others = {}
+    if not args.no_other_configs and args.workload == "lm":
+        for name, heads, rows in OTHER_CONFIGS:  # inputs and oracle time before any GPU work
+            wo = WORKLOADS[name]
+            inp = make_inputs(wo)
+            others[name] = (wo, inp, None if args.no_cpu_baseline else cpu_baseline(wo, *inp, heads=heads,
+                                                                                      rows_per_head=rows))
 
     import torch
 
@@ -481,9 +523,54 @@ def main():
     if not args.no_ceiling and w.dtype == "bf16":
         pr = simd_probes([0], stream)
         res["mfma_ceiling"] = {"mfma_only_tflops": pr[0]["tflops"], "frac_of_mfma_only": round(tflops / pr[0]["tflops"], 4)}
+    if others:
+        del qd, kd, vd, out, lse
+        torch.cuda.empty_cache()
+        res["other_configs"] = {name: other_config_leg(wo, inp, ocpu, args, stream)
+                                for name, (wo, inp, ocpu) in others.items()}
     if cpu is not None:
         res["cpu_baseline"] = cpu
     print(json.dumps(res), flush=True)
+
+
+def other_config_leg(w, inp, cpu, args, stream):
+    """csa_forward and std_fwd on another bf16 configuration (same FLOP convention as the
+    metric), with the oracle's time on a sample of its rows."""
+    import torch
+
+    import continuous_softmax_attention_amd as csa
+
+    dev = torch.device("cuda:0")
+    q, k, v, k0, v0 = inp
+    qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
+    k0d = None if k0 is None else k0.to(dev)
+    v0d = None if v0 is None else v0.to(dev)
+    out = torch.empty_like(qd)
+    lse = torch.empty((w.B, w.H, w.T), dtype=torch.float32, device=dev)
+
+    def step():
+        csa.csa_forward(qd, kd, vd, k0d, v0d, out=out, lse=lse, stream=stream)
+
+    def std_step():
+        csa.std_fwd(qd, kd, vd, out=out, lse=lse, stream=stream)
+
+    avg, mn, _ = time_kernel(step, args.steps, args.warmup, stream)
+    s_avg, _, _ = time_kernel(std_step, args.steps, args.warmup, stream)
+    flop = float(w.flop)
+    tf, s_tf = flop / (avg * 1e-3) / 1e12, flop / (s_avg * 1e-3) / 1e12
+    leg = {"workload": f"{w.name}: causal CSA forward B{w.B} H{w.H} T{w.T} d{w.d} {w.dtype}"
+                       + f", q scaled by {w.q_scale * math.sqrt(w.d):g}/sqrt(d)"
+                       + f", k0/v0 {w.sink}",
+           "value": round(tf, 2), "unit": "TFLOP/s", "pct_peak": round(100.0 * tf / PEAK_BF16_TFLOPS, 2),
+           "frac": round(tf / PEAK_BF16_TFLOPS, 4), "kernel_ms": {"avg": round(avg, 4), "min": round(mn, 4)},
+           "std_attention": {"value": round(s_tf, 2), "kernel_ms": round(s_avg, 4)},
+           "ratio_vs_std": round(tf / s_tf, 4), "flop": flop}
+    if cpu is not None:
+        leg["cpu_baseline"] = cpu
+        leg["gpu_over_oracle"] = round(tf / cpu["value"], 1)
+    del qd, kd, vd, out, lse
+    torch.cuda.empty_cache()
+    return leg
 
 
 if __name__ == "__main__":

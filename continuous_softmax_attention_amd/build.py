@@ -24,9 +24,13 @@ LIBS = {
 }
 
 # -packed-fp32-ops: no v_pk_{add,mul,fma}_f32 in the generated code.
-# -fno-honor-nans: no kernel produces or tests a NaN on purpose; without it every fmaxf
-# on a value the compiler cannot prove canonical (MFMA results, cross-lane moves) gets
-# an extra v_max_f32 x, x to quiet signalling NaNs.
+# -fno-honor-nans: without it every fmaxf on a value the compiler cannot prove canonical
+# (MFMA results, cross-lane moves) gets an extra v_max_f32 x, x to quiet signalling NaNs.
+# One NaN does arise by design: where two neighbouring logits are exactly equal the
+# reciprocal of their difference is infinite and the closed-form edge terms are 0 * inf;
+# a select on |difference| < threshold (compare, then v_cndmask) always discards that value
+# for the series form, and no NaN is compared, maximised or stored.  Exactly-equal-logit
+# cases run through the kernels in the tests (q = 0: the trapezoid closed form, fp32 and bf16).
 HIPCC_FLAGS = [
     "--offload-arch=gfx950",
     "-O3",

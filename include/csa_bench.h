@@ -46,6 +46,12 @@ int std_fwd_check(const void* q, const void* k, const void* v, const void* out, 
  *           neighbour difference, reciprocal, both edge terms with the Taylor select)
  *   kind 7  kinds 6 and 0 together (two 16x16x32 MFMAs per key, the forward's ratio)
  *   kind 8  kinds 6 and 5 together (the same FLOP on 32x32x16 MFMAs)
+ *   kind 9  the weights of kind 6 by the log-domain route (eq. (13): b as the log of the sum of
+ *           the two phi_2 terms, each phi_2 in logs, log-sum-exp, then exp), two keys per iteration
+ *   kind 10 kind 1 with 2 v_exp_f32 chains beside the 8 FMA chains
+ *   kind 11 kind 1 with 2 v_rcp_f32 chains beside the 8 FMA chains
+ *   kind 12 the weights of kind 6 with the reciprocal replaced by a 1024-entry LDS table
+ *           lookup (one ds_read_b128 and two fmas per edge; placeholder table values)
  *   sink    device, >= ceil(waves / 4) floats: one result per work-group (keeps the work)
  *   cycles  device, 1 uint64, zeroed by the caller: raised (atomic max) to the shader-clock
  *           cycles (s_memtime) of the longest-running wave's loop

@@ -45,7 +45,7 @@ def test_header_declares_the_entry_points():
 
 def test_probe_rejects_bad_arguments_before_launching():
     # unknown kind, sizes out of range, null buffers: refused before any HIP call
-    for kind, waves, iters, sink, cyc in ((-1, 64, 1, A, A), (9, 64, 1, A, A), (0, 0, 1, A, A),
+    for kind, waves, iters, sink, cyc in ((-1, 64, 1, A, A), (13, 64, 1, A, A), (0, 0, 1, A, A),
                                           (0, 1 << 25, 1, A, A), (0, 64, 0, A, A), (0, 64, 1 << 31, A, A),
                                           (0, 64, 1, None, A), (0, 64, 1, A, None)):
         assert csa.csa_probe_raw(kind, waves, iters, sink, cyc) == INV

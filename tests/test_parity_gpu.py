@@ -142,6 +142,23 @@ def test_trapezoid_closed_form_through_kernel():
         assert abs(lse[0, 0, r] - math.log(t)) < 1e-5
 
 
+def test_trapezoid_closed_form_through_kernel_bf16():
+    # the bf16 kernel on exactly equal logits (every neighbour difference 0: the reciprocal of
+    # the difference is infinite there and only the series branch's value may reach a weight)
+    T, d = 200, 128
+    _, k, v, k0, v0 = _random_case(1, 2, T, d, torch.bfloat16, seed=4)
+    q = torch.zeros(1, 2, T, d, dtype=torch.bfloat16)
+    o, lse = _run(q, k, v, k0, v0)
+    assert np.isfinite(o).all() and np.isfinite(lse).all()
+    for h in range(2):
+        vh = torch.cat([v0[0, h][None], v[0, h]]).double().numpy()
+        for r in range(T):
+            t = r + 1
+            expect = (0.5 * vh[0] + vh[1:t].sum(0) + 0.5 * vh[t]) / t
+            assert np.abs(o[0, h, r] - expect).max() < 1e-2  # bf16 output rounding
+            assert abs(lse[0, h, r] - math.log(t)) < 4e-3      # row sum of bf16-rounded weights
+
+
 def test_linear_ramp_closed_form_through_kernel():
     # k_i = i w, v_i = i c, k_0 = v_0 = 0: o_t = c (e^{bt}(bt-1)+1)/(b(e^{bt}-1)), lse = ln((e^{bt}-1)/b)
     T, d, beta = 100, 16, 0.013
@@ -183,6 +200,26 @@ def test_std_comparator_matches_softmax_attention(T, dtype):
     eo = float(np.abs(o.float().cpu().double().numpy() - o_ref).max())
     el = float(np.abs(lse.cpu().double().numpy() - l_ref).max())
     assert eo <= TOL[dtype] and el <= TOL[dtype], (eo, el)
+
+
+@pytest.mark.parametrize("name", ["lm", "stress"])
+def test_std_comparator_at_workload_size_sampled_rows(name):
+    # the comparator at the size the bench times it (the ratio to it is part of the headline):
+    # every row finite, sampled rows against float64 eq. (12)
+    w = WORKLOADS[name]
+    print(f"[parity std] {name}: B{w.B} H{w.H} T{w.T} d{w.d} {w.dtype}", flush=True)
+    q, k, v, _, _ = make_inputs(w)
+    o_dev, lse_dev = csa.std_fwd(*_gpu(q, k, v))
+    torch.cuda.synchronize()
+    assert bool(torch.isfinite(lse_dev).all()) and bool(torch.isfinite(o_dev.float()).all())
+    rows = sample_rows(w.T, seed=w.seed + 1, n_random=16)
+    o = o_dev[:, :, rows].float().cpu().double().numpy()
+    lse = lse_dev[:, :, rows].cpu().double().numpy()
+    del o_dev, lse_dev
+    o_ref, l_ref = std_reference(q, k, v, rows=rows)
+    eo, el = _errs(o, lse, o_ref, l_ref)
+    _report(f"std {name} ({len(rows)} rows x {w.B * w.H} heads)", eo, el)
+    assert eo <= TOL[q.dtype] and el <= TOL[q.dtype]
 
 
 def test_invalid_arguments_raise_on_gpu():

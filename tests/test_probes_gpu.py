@@ -14,7 +14,7 @@ import continuous_softmax_attention_amd as csa
 
 pytestmark = pytest.mark.gpu
 DEV = torch.device("cuda:0")
-KINDS = range(9)  # include/csa_bench.h: kinds 0 .. 8
+KINDS = range(13)  # include/csa_bench.h: kinds 0 .. 12
 
 
 @pytest.mark.parametrize("kind", KINDS)

@@ -27,6 +27,8 @@
 // Kernels (one launch each, in this order on the caller's stream):
 //   bwd_pre   D_t = dO_t . o_t and mu_t into the workspace; zero rows standing in for a
 //             null k_0 / v_0.
+//   bwd_transpose  Q^T and dO^T ([B*H][D][T rounded up to 128], zeros past T) into the
+//             workspace: the A operands of bwd_dkdv's dK / dV products.
 //   bwd_dq    one work-group per 128 query rows (the forward's decomposition: 8 waves x
 //             16 queries, 64-key tiles double-buffered in LDS).  Per tile S^T = K Q^T and
 //             dP^T = V dO^T on MFMAs, plus one 16-row "halo" block whose rows 0 and 1 are
@@ -38,7 +40,8 @@
 //             row ranges per (b, h), then their fixed-order sum (skipped when both are null).
 //   bwd_dkdv  one work-group per 64 key rows, looping over 128-row query tiles: the same
 //             S^T, dP^T, P and dS per wave; P and dS (bf16) go through LDS so that
-//             dV^T += dO^T P and dK^T += Q^T dS contract over queries on MFMAs.
+//             dV^T += dO^T P and dK^T += Q^T dS contract over queries on MFMAs, with Q^T and
+//             dO^T read from the transposed copies (two work-groups per CU).
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -83,6 +86,15 @@ __device__ __forceinline__ int64_t ds_tile_index(int qb, int kb) { return (int64
 // B*H x 16 chunks x 2 x 128 (sized for d = 128 whatever d is).
 constexpr int kBwdZeroBytes = 512;
 
+// Then, 256-byte aligned, Q^T and dO^T of every head: [B*H][D][Tp] bf16 with Tp = T rounded up
+// to a multiple of 128 and zeros past T (written by bwd_transpose, read by bwd_dkdv as the
+// operands of its dK / dV products).
+constexpr int kSinkChunks = 16;
+__host__ __device__ constexpr int64_t bwd_tp(int64_t T) { return (T + 127) / 128 * 128; }
+__host__ __device__ constexpr int64_t bwd_qt_offset(int64_t BH, int64_t T) {
+  return (kBwdZeroBytes + 16 * BH * T + BH * kSinkChunks * 2 * 128 * 4 + 255) / 256 * 256;
+}
+
 struct BwdWs {
   const char* zero;
   float* delta;
@@ -90,11 +102,14 @@ struct BwdWs {
   float* ds0;
   float* p0;
   float* sink;
+  bf16* qt;   // Q^T [B*H][D][Tp]
+  bf16* dot;  // dO^T [B*H][D][Tp]
 };
-__device__ __forceinline__ BwdWs bwd_ws(char* ws, int BH, int T) {
+__device__ __forceinline__ BwdWs bwd_ws(char* ws, int BH, int T, int D) {
   const size_t n = (size_t)BH * (size_t)T;
   float* f = (float*)(ws + kBwdZeroBytes);
-  return {ws, f, f + n, f + 2 * n, f + 3 * n, f + 4 * n};
+  bf16* qt = (bf16*)(ws + bwd_qt_offset(BH, T));
+  return {ws, f, f + n, f + 2 * n, f + 3 * n, f + 4 * n, qt, qt + (size_t)BH * D * bwd_tp(T)};
 }
 
 constexpr float kMuShift = -1.0575327458897954f;  // 2 log2(ln 2)
@@ -223,24 +238,38 @@ __device__ __forceinline__ void edge_grad(float al, float pl, float ar, float pr
   }
 }
 
-// P and dS of one lane's 16 consecutive keys base+t of its query.  s/dp: logits and dO.v
+// P and dS of one lane's 16 consecutive keys base+t of its query, rounded to bf16 (to nearest
+// even) as they are formed: P8[h][e], dS8[h][e] for key base + 8h + e.  s/dp: logits and dO.v
 // of those keys; sl, dpl and sr, dpr: the same for keys base-1 and base+16.  Key base+t is
-// visible iff t <= lim.  Also returns P and dS of key base-1 as they follow from its right
-// edge alone: exact when key base-1 is position 0 (which has no left edge).  MASKED = false
-// when every key of the tile and its right neighbour are visible (lim >= 16 in every lane).
-template <bool MASKED>
+// visible iff t <= lim.  Also returns P and dS of key base-1 (float) as they follow from its
+// right edge alone: exact when key base-1 is position 0 (which has no left edge).
+// MASKED = false when every key of the tile and its right neighbour are visible (lim >= 16 in
+// every lane).
+template <bool MASKED, typename Emit>
 __device__ __forceinline__ void tile_grad(const float (&s)[16], const float (&dp)[16], float sl, float dpl,
-                                          float sr, float dpr, float mu, float delta, int lim, float (&P)[16],
-                                          float (&dS)[16], float& p_left, float& ds_left) {
+                                          float sr, float dpr, float mu, float delta, int lim, Emit&& emit,
+                                          float& p_left, float& ds_left) {
 #pragma clang fp contract(off)
-  auto alpha = [&](float x) { return __builtin_fmaf(x, kLog2e, -mu); };
-  float aC = alpha(sl), pC = exp2_fast(aC), dC = dpl;
-  float aN = alpha(s[0]), pN = exp2_fast(aN), dN = dp[0];
+  bf16x8 P8, dS8;
+  // Opaque copies of the inputs: callers inline the masked and the unmasked form behind one
+  // branch, and without them the compiler computed everything the two forms share (every
+  // exponential and difference of the tile) above the branch, all live at once (spills).
+  float mu_o = mu, delta_o = delta, dpl_o = dpl, dpr_o = dpr;
+  asm volatile("" : "+v"(mu_o), "+v"(delta_o), "+v"(dpl_o), "+v"(dpr_o));
+  float dpo[16];
+#pragma unroll
+  for (int t = 0; t < 16; ++t) {
+    dpo[t] = dp[t];
+    asm volatile("" : "+v"(dpo[t]));
+  }
+  auto alpha = [&](float x) { return __builtin_fmaf(x, kLog2e, -mu_o); };
+  float aC = alpha(sl), pC = exp2_fast(aC), dC = dpl_o;
+  float aN = alpha(s[0]), pN = exp2_fast(aN), dN = dpo[0];
   float W, L, C;
   edge_grad<MASKED>(aC, pC, aN, pN, 0 <= lim, 0.0f, W, L, C);
   float G = C * (dC - dN);
   p_left = W;
-  ds_left = __builtin_fmaf(W, dC - delta, -G);
+  ds_left = __builtin_fmaf(W, dC - delta_o, -G);
   float Lprev = L, Gprev = G;
   aC = aN;
   pC = pN;
@@ -249,16 +278,18 @@ __device__ __forceinline__ void tile_grad(const float (&s)[16], const float (&dp
   for (int t = 0; t < 16; ++t) {
     if (t < 15) {
       aN = alpha(s[t + 1]);
-      dN = dp[t + 1];
+      dN = dpo[t + 1];
     } else {
       aN = alpha(sr);
-      dN = dpr;
+      dN = dpr_o;
     }
     pN = exp2_fast(aN);
     edge_grad<MASKED>(aC, pC, aN, pN, t + 1 <= lim, Lprev, W, L, C);
     G = C * (dC - dN);
-    P[t] = W;
-    dS[t] = __builtin_fmaf(W, dC - delta, Gprev - G);
+    P8[t & 7] = (bf16)W;
+    dS8[t & 7] = (bf16)__builtin_fmaf(W, dC - delta_o, Gprev - G);
+    if ((t & 7) == 7) emit(t >> 3, P8, dS8);  // keys 8h .. 8h + 7 done
+    if ((t & 3) == 3) __builtin_amdgcn_sched_barrier(0);  // bounds how far work is hoisted (registers)
     Lprev = L;
     Gprev = G;
     aC = aN;
@@ -311,6 +342,7 @@ __device__ __forceinline__ void logits_tile(CSA_LDS const char* tile, CSA_LDS co
 #pragma unroll
     for (int st = 0; st < NSTEP; ++st)
       S[blk] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(row_read(tile, kbase, st, blk), b[st], S[blk], 0, 0, 0);
+    __builtin_amdgcn_sched_barrier(0);  // one block's operands in flight at a time (register pressure)
   }
   H = f32x4{};
 #pragma unroll
@@ -386,7 +418,7 @@ __global__ void __launch_bounds__(256) bwd_pre_kernel(BwdParams p) {
   constexpr int CH = D / 8;
   constexpr int RPW = 64 / CH;  // rows per wave
   const int BH = p.B * p.H, T = p.T;
-  const BwdWs w = bwd_ws(p.ws, BH, T);
+  const BwdWs w = bwd_ws(p.ws, BH, T, D);
   if (blockIdx.x == 0 && threadIdx.x < kBwdZeroBytes / 4) ((float*)p.ws)[threadIdx.x] = 0.0f;
   const int lane = threadIdx.x & 63;
   const int64_t nrows = (int64_t)BH * T;
@@ -434,7 +466,7 @@ __global__ void __launch_bounds__(512, 2) bwd_dq_kernel(BwdParams p) {
   const bool wave_rows = qw < Tn;
   const int jw = wave_rows ? min(qw + 15, Tn - 1) / kTile : -1;
   const int jmax = min(q0 + kBlockRows - 1, Tn - 1) / kTile;
-  const BwdWs ws = bwd_ws(p.ws, BH, Tn);
+  const BwdWs ws = bwd_ws(p.ws, BH, Tn, D);
 
   const size_t head = (size_t)bh * (size_t)Tn * D;
   const char* Kg = (const char*)((const bf16*)p.k + head);
@@ -503,23 +535,22 @@ __global__ void __launch_bounds__(512, 2) bwd_dq_kernel(BwdParams p) {
       neighbours(s, Hs, n, g, sl, sr);
       neighbours(dp, Hd, n, g, dl, dr);
       int lim = qr < Tn ? qr - (j * kTile + 16 * g) : -2;
-      float P[16], dS[16], pl, dsl;
+      bf16x8 dS8[2];
+      float pl, dsl;
+      auto keep = [&](int h, const bf16x8&, const bf16x8& ds) { dS8[h] = ds; };
       // every edge of the tile exists for every query of the wave (rows past T only feed
       // their own, unstored, dq rows)
-      if ((j + 1) * kTile <= qw) tile_grad<false>(s, dp, sl, dl, sr, dr, mu, delta, lim, P, dS, pl, dsl);
-      else tile_grad<true>(s, dp, sl, dl, sr, dr, mu, delta, lim, P, dS, pl, dsl);
+      if ((j + 1) * kTile <= qw) tile_grad<false>(s, dp, sl, dl, sr, dr, mu, delta, lim, keep, pl, dsl);
+      else tile_grad<true>(s, dp, sl, dl, sr, dr, mu, delta, lim, keep, pl, dsl);
       if (j == 0) {
         p0 = pl;
         ds0 = dsl;
       }
 #pragma unroll
       for (int c = 0; c < 2; ++c) {
-        bf16x8 B;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) B[e] = (bf16)dS[8 * c + e];
 #pragma unroll
         for (int mb = 0; mb < NMB; ++mb)
-          acc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(tr_read(b + TILE, vbase, c, mb), B, acc[mb], 0, 0, 0);
+          acc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(tr_read(b + TILE, vbase, c, mb), dS8[c], acc[mb], 0, 0, 0);
       }
     }
     wait_vmem();
@@ -579,7 +610,7 @@ __global__ void __launch_bounds__(512, 2) bwd_dq_from_ds_kernel(BwdParams p) {
   const bool wave_rows = qw < Tn;
   const int jw = wave_rows ? min(qw + 15, Tn - 1) / kTile : -1;
   const int jmax = min(q0 + kBlockRows - 1, Tn - 1) / kTile;
-  const BwdWs ws = bwd_ws(p.ws, BH, Tn);
+  const BwdWs ws = bwd_ws(p.ws, BH, Tn, D);
 
   const size_t head = (size_t)bh * (size_t)Tn * D;
   const char* Kg = (const char*)((const bf16*)p.k + head);
@@ -642,7 +673,6 @@ __global__ void __launch_bounds__(512, 2) bwd_dq_from_ds_kernel(BwdParams p) {
 // work-groups per (b, h) each sum a contiguous range of query rows into float32 partials
 // in the workspace; one work-group per (b, h) adds the partials (fixed order: the result
 // does not depend on scheduling) and rounds once.
-constexpr int kSinkChunks = 16;
 
 template <int D>
 __global__ void __launch_bounds__(256) bwd_sink_partial_kernel(BwdParams p) {
@@ -650,7 +680,7 @@ __global__ void __launch_bounds__(256) bwd_sink_partial_kernel(BwdParams p) {
   constexpr int NPH = 256 / CH;  // row phases
   __shared__ float red[2][NPH][D];
   const int BH = p.B * p.H, Tn = p.T;
-  const BwdWs ws = bwd_ws(p.ws, BH, Tn);
+  const BwdWs ws = bwd_ws(p.ws, BH, Tn, D);
   const int bh = blockIdx.x / kSinkChunks, chunk = blockIdx.x % kSinkChunks;
   const int rows = (Tn + kSinkChunks - 1) / kSinkChunks;
   const int t0 = chunk * rows, t1 = min(Tn, t0 + rows);
@@ -685,7 +715,7 @@ __global__ void __launch_bounds__(256) bwd_sink_partial_kernel(BwdParams p) {
 template <int D>
 __global__ void __launch_bounds__(256) bwd_sink_final_kernel(BwdParams p) {
   const int BH = p.B * p.H;
-  const BwdWs ws = bwd_ws(p.ws, BH, p.T);
+  const BwdWs ws = bwd_ws(p.ws, BH, p.T, D);
   const int bh = blockIdx.x;
   if (threadIdx.x < 2 * D) {
     const int which = threadIdx.x / D, d = threadIdx.x % D;
@@ -696,23 +726,63 @@ __global__ void __launch_bounds__(256) bwd_sink_final_kernel(BwdParams p) {
   }
 }
 
+// Q^T and dO^T of every head into the workspace ([B*H][D][Tp] bf16, zeros past T): one
+// work-group per (head, 64-row tile, tensor) stages the rows in LDS at a pitch of D/2 + 1 words
+// (the 8 rows one lane reads for a column fall on distinct banks across the wave) and writes 8
+// consecutive rows of one column per lane, 8 lanes covering one column's 128 bytes.
+template <int D>
+__global__ void __launch_bounds__(256) bwd_transpose_kernel(BwdParams p) {
+  constexpr int PW = D / 2 + 1;  // words per staged row
+  __shared__ unsigned buf[64 * PW];
+  const int BH = p.B * p.H, Tn = p.T;
+  const int Tp = (int)bwd_tp(Tn), ntile = Tp / 64;
+  const int which = blockIdx.x & 1, tile = (blockIdx.x >> 1) % ntile, bh = (blockIdx.x >> 1) / ntile;
+  const BwdWs ws = bwd_ws(p.ws, BH, Tn, D);
+  const bf16* src = (const bf16*)(which ? p.dout : p.q) + (size_t)bh * Tn * D;
+  for (int i = threadIdx.x; i < 64 * D / 8; i += 256) {
+    const int r = i / (D / 8), c = i % (D / 8), t = tile * 64 + r;
+    uint4 v = {0u, 0u, 0u, 0u};
+    if (t < Tn) v = *(const uint4*)(src + (size_t)t * D + 8 * c);
+    unsigned* w = buf + r * PW + 4 * c;
+    w[0] = v.x;
+    w[1] = v.y;
+    w[2] = v.z;
+    w[3] = v.w;
+  }
+  __syncthreads();
+  bf16* dst = (which ? ws.dot : ws.qt) + (size_t)bh * D * Tp + tile * 64;
+  const bf16* sb = (const bf16*)buf;
+  for (int i = threadIdx.x; i < D * 8; i += 256) {
+    const int tc = i & 7, dcol = i >> 3;
+    bf16x8 o;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[e] = sb[(8 * tc + e) * (2 * PW) + dcol];
+    *(bf16x8*)(dst + (size_t)dcol * Tp + 8 * tc) = o;
+  }
+}
+
+// dK and dV: one work-group (8 waves) per 64 key rows, looping over the 128-row query blocks
+// from the key block on.  Per block each wave forms S^T and dP^T of its 16 queries on the
+// MFMAs (K, V and the halo rows staged once in LDS), then P and dS (tile_grad), which go to
+// LDS in the transposed layout; after a barrier dK^T += Q^T dS and dV^T += dO^T P contract
+// over the block's 128 queries on the MFMAs, wave w owning d-block w % (D/16) of dK and dV
+// for KPW 16-key blocks.  The A operands Q^T, dO^T come from the transposed copies in the
+// workspace (16 contiguous bytes per lane), so the work-group holds only K, V, halo, P and dS
+// in LDS (73 KiB at d = 128) and two work-groups share a CU: four waves per SIMD.
 // WRITE_DS: also store this wave's dS into its dS tile (for bwd_dq_from_ds) and, for the
 // first key block, P and dS of position 0 (for the k_0 / v_0 gradients and dq's k_0 term).
 template <int D, bool WRITE_DS>
-__global__ void __launch_bounds__(512, 2) bwd_dkdv_kernel(BwdParams p) {
+__global__ void __launch_bounds__(512, 4) bwd_dkdv_kernel(BwdParams p) {
   using WT = WaveTile<D>;
-  constexpr int CH = WT::CH, ROWB = WT::ROWB, NSTEP = WT::NSTEP, NMB = WT::NMB;
+  constexpr int ROWB = WT::ROWB, NSTEP = WT::NSTEP, NMB = WT::NMB;
   constexpr int TILE = WT::TILE, HALO = WT::HALO;
+  constexpr int CH = WT::CH;
   constexpr int PT = 2 * 64 * 128;  // P or dS: 128 queries x 64 keys bf16 (two 64-row tiles)
-  // Krow | Vrow | Khalo | Vhalo | Q (2 tiles) | dO (2 tiles) | P | dS
-  constexpr int OFF_V = TILE, OFF_KH = 2 * TILE, OFF_VH = 2 * TILE + HALO, OFF_Q = 2 * TILE + 2 * HALO;
-  constexpr int OFF_DO = OFF_Q + 2 * TILE, OFF_P = OFF_DO + 2 * TILE, OFF_DS = OFF_P + PT;
+  // Krow | Vrow | Khalo | Vhalo | P | dS
+  constexpr int OFF_V = TILE, OFF_KH = 2 * TILE, OFF_VH = 2 * TILE + HALO, OFF_P = 2 * TILE + 2 * HALO;
+  constexpr int OFF_DS = OFF_P + PT;
   constexpr int LDS_BYTES = OFF_DS + PT;
-  // output blocks per wave: MPW 16-column d-blocks x KPW 16-key blocks (2 x 2 at d = 128: of the
-  // splits of 4 blocks per wave it reads the fewest operands from LDS -- 8 transposed reads per
-  // 32-query step against 10 for 1 x 4)
-  constexpr int MPW = NMB == 8 ? 2 : 1;
-  constexpr int KPW = 2;
+  constexpr int KPW = 4 * NMB / 8;  // 16-key blocks per wave: 4 at d = 128, 2 at d = 64
   static_assert(D == 64 || D == 128, "head dimension");
 
   __shared__ __attribute__((aligned(1024))) char smem[LDS_BYTES];
@@ -723,14 +793,13 @@ __global__ void __launch_bounds__(512, 2) bwd_dkdv_kernel(BwdParams p) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n = lane & 15, g = lane >> 4;
   const int Tn = p.T, BH = p.B * p.H;
-  // heads four at a time per XCD, key block 0 (the most queries) first: against heads-fastest
-  // order, fetched bytes per lm launch 1285 -> 458 MB with two heads at a time and 1.3% faster;
-  // four at a time is 1.4% faster again (one at a time: 1% slower than two)
+  const int Tp = (int)bwd_tp(Tn);
+  // heads four at a time per XCD, key block 0 (the most queries) first
   int bhl, kb;
   xcd_head_order<4>(blockIdx.x, p.nh, (Tn + kTile - 1) / kTile, bhl, kb);
   const int bh = p.h0 + bhl;
   const int J = kb * kTile;
-  const BwdWs ws = bwd_ws(p.ws, BH, Tn);
+  const BwdWs ws = bwd_ws(p.ws, BH, Tn, D);
 
   const size_t head = (size_t)bh * (size_t)Tn * D;
   const char* Kg = (const char*)((const bf16*)p.k + head);
@@ -744,7 +813,7 @@ __global__ void __launch_bounds__(512, 2) bwd_dkdv_kernel(BwdParams p) {
     const int which = i / (14 * CH), chunk = i % (14 * CH);
     *(CSA_LDS f32x4*)(lds + OFF_KH + which * HALO + halo_zero_off<D>(chunk)) = f32x4{};
   }
-  const int roff = row_layout_src<ROWB>(tid), toff = tr_layout_src<ROWB>(tid);
+  const int roff = row_layout_src<ROWB>(tid);
   // the key block and its halo rows, once
   stage_tile<D>(lds, Kg, J, roff, Tn, wave);
   stage_tile<D>(lds + OFF_V, Vg, J, roff, Tn, wave);
@@ -755,18 +824,20 @@ __global__ void __launch_bounds__(512, 2) bwd_dkdv_kernel(BwdParams p) {
   }
 
   const int kbase = row_kbase(n, g);
-  int vbase[2], pbase[2][4];
+  int vbase[2];
   tr_vbase(n, g, vbase);
-  ptr_bases(vbase, pbase);
   const int hoff = n * WT::HROW + 16 * g;
-  // this wave's output blocks: d-blocks mb0 .. mb0 + MPW - 1, 16-key blocks kc0 .. kc0 + KPW - 1
-  const int mb0 = MPW * (wave & 3);
-  const int kc0 = KPW * (wave >> 2);
-  f32x4 dK[MPW][KPW], dV[MPW][KPW];
+  // this wave's output blocks: d-block mb, 16-key blocks kc0 .. kc0 + KPW - 1
+  const int mb = wave % NMB;
+  const int kc0 = KPW * (wave / NMB);
+  f32x4 dK[KPW], dV[KPW];
 #pragma unroll
-  for (int a = 0; a < MPW; ++a)
-#pragma unroll
-    for (int i = 0; i < KPW; ++i) dK[a][i] = dV[a][i] = f32x4{};
+  for (int i = 0; i < KPW; ++i) dK[i] = dV[i] = f32x4{};
+  // A operands of the dK / dV products: row 16 mb + n of Q^T / dO^T, 8 queries per lane group
+  // (uniform bases and 32-bit per-lane offsets: one VGPR per address)
+  const bf16* qt_head = ws.qt + (size_t)bh * D * Tp;
+  const bf16* dot_head = ws.dot + (size_t)bh * D * Tp;
+  const int row_off = (16 * mb + n) * Tp;
 
   // P / dS rows of this wave in LDS: query tile row 16 wave + n = tile (wave >> 2), row 16 (wave & 3) + n
   const int prow = 16 * (wave & 3) + n;
@@ -774,97 +845,83 @@ __global__ void __launch_bounds__(512, 2) bwd_dkdv_kernel(BwdParams p) {
 
   const int i0 = J / kBlockRows;
   const int i1 = (Tn - 1) / kBlockRows;
-  // this wave's query rows of block `it` in registers (the logits' operands) with mu, delta
-  bf16x8 qreg[NSTEP], dreg[NSTEP];
-  float mu_n, delta_n;
-  auto load_rows = [&](int it) {
-    const int rowc = min(it * kBlockRows + 16 * wave + n, Tn - 1);
-#pragma unroll
-    for (int s = 0; s < NSTEP; ++s) {
-      qreg[s] = *(const bf16x8*)(Qg + (size_t)rowc * ROWB + (4 * s + g) * 16);
-      dreg[s] = *(const bf16x8*)(Og + (size_t)rowc * ROWB + (4 * s + g) * 16);
-    }
-    mu_n = ws.mu[(size_t)bh * Tn + rowc];
-    delta_n = ws.delta[(size_t)bh * Tn + rowc];
-  };
-  load_rows(i0);
-  wait_vmem();  // the key block, its halo and the first rows
+  wait_vmem();  // the key block and its halo
   __syncthreads();
-  // Per block: the logits from the registers first; then the copies of the block's Q and dO
-  // tiles (for dK, dV) and the loads of the next block's rows, both in flight during the
-  // VALU work of the gradients (a wait for the rows would otherwise wait for the copies
-  // issued before them as well: loads complete in order).
   for (int it = i0; it <= i1; ++it) {
     const int Q0 = it * kBlockRows;
     const int qr = Q0 + 16 * wave + n;
+    // this wave's query rows (the logits' B operands), one tensor at a time (registers)
+    const int rowc = min(qr, Tn - 1);
     float s[16], dp[16];
     f32x4 Hs, Hd;
-    logits_tile<D>(lds, lds + OFF_KH, kbase, hoff, qreg, s, Hs);
-    logits_tile<D>(lds + OFF_V, lds + OFF_VH, kbase, hoff, dreg, dp, Hd);
-    const float mu = mu_n, delta = delta_n;
-    // both 64-row halves always (rows past T repeat row T-1): the dK / dV products read
-    // all 128 rows, with P = dS = 0 on rows past T
-    stage_tile<D>(lds + OFF_Q, Qg, Q0, toff, Tn, wave);
-    stage_tile<D>(lds + OFF_Q + TILE, Qg, Q0 + kTile, toff, Tn, wave);
-    stage_tile<D>(lds + OFF_DO, Og, Q0, toff, Tn, wave);
-    stage_tile<D>(lds + OFF_DO + TILE, Og, Q0 + kTile, toff, Tn, wave);
-    if (it < i1) load_rows(it + 1);
+    {
+      bf16x8 qreg[NSTEP];
+#pragma unroll
+      for (int st = 0; st < NSTEP; ++st) qreg[st] = *(const bf16x8*)(Qg + (rowc * ROWB + (4 * st + g) * 16));
+      logits_tile<D>(lds, lds + OFF_KH, kbase, hoff, qreg, s, Hs);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    {
+      bf16x8 dreg[NSTEP];
+#pragma unroll
+      for (int st = 0; st < NSTEP; ++st) dreg[st] = *(const bf16x8*)(Og + (rowc * ROWB + (4 * st + g) * 16));
+      logits_tile<D>(lds + OFF_V, lds + OFF_VH, kbase, hoff, dreg, dp, Hd);
+    }
+    const float mu = (ws.mu + (size_t)bh * Tn)[rowc];
+    const float delta = (ws.delta + (size_t)bh * Tn)[rowc];
     float sl, sr, dl, dr;
     neighbours(s, Hs, n, g, sl, sr);
     neighbours(dp, Hd, n, g, dl, dr);
     const int lim = qr < Tn ? qr - (J + 16 * g) : -2;
-    float P[16], dS[16], pl, dsl;
-    // every edge exists for every query of the wave, and no row of the wave lies past T
-    // (those rows must contribute zeros to dK and dV)
-    const int qw = Q0 + 16 * wave;
-    if (qw >= J + kTile && qw + 15 < Tn) tile_grad<false>(s, dp, sl, dl, sr, dr, mu, delta, lim, P, dS, pl, dsl);
-    else tile_grad<true>(s, dp, sl, dl, sr, dr, mu, delta, lim, P, dS, pl, dsl);
-    // keys 16g + 8h + e = chunks 2g + h of the P / dS row
-    char* dst = nullptr;
-    if constexpr (WRITE_DS) {
-      dst = p.ds + ((size_t)bhl * (size_t)p.ds_tiles + (size_t)ds_tile_index(it, kb)) * kDsTileBytes +
-            (size_t)(wave * 64 + lane) * 32;
-      if (J == 0 && g == 0 && qr < Tn) {
-        ws.p0[(size_t)bh * Tn + qr] = pl;
-        ws.ds0[(size_t)bh * Tn + qr] = dsl;
-      }
-    }
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      bf16x8 pv, dv;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        pv[e] = (bf16)P[8 * h + e];
-        dv[e] = (bf16)dS[8 * h + e];
-      }
+    float pl, dsl;
+    // keys 16g + 8h + e = chunks 2g + h of the P / dS row: to LDS (and dS to its tile) as soon
+    // as the 8 keys of a half are done
+    auto emit = [&](int h, const bf16x8& pv, const bf16x8& dv) {
       const int at = pt_off + ptr_layout_at(prow, 2 * g + h);
       *(CSA_LDS bf16x8*)(lds + OFF_P + at) = pv;
       *(CSA_LDS bf16x8*)(lds + OFF_DS + at) = dv;
-      if constexpr (WRITE_DS) *(bf16x8*)(dst + 16 * h) = dv;
+      if constexpr (WRITE_DS)  // uniform tile base, 32-bit lane offset
+        *(bf16x8*)(p.ds + ((size_t)bhl * (size_t)p.ds_tiles + (size_t)ds_tile_index(it, kb)) * kDsTileBytes +
+                   ((wave * 64 + lane) * 32 + 16 * h)) = dv;
+    };
+    // every edge exists for every query of the wave, and no row of the wave lies past T
+    // (those rows must contribute zeros to dK and dV)
+    const int qw = Q0 + 16 * wave;
+    if (qw >= J + kTile && qw + 15 < Tn) tile_grad<false>(s, dp, sl, dl, sr, dr, mu, delta, lim, emit, pl, dsl);
+    else tile_grad<true>(s, dp, sl, dl, sr, dr, mu, delta, lim, emit, pl, dsl);
+    if constexpr (WRITE_DS) {
+      if (J == 0 && g == 0 && qr < Tn) {
+        (ws.p0 + (size_t)bh * Tn)[qr] = pl;
+        (ws.ds0 + (size_t)bh * Tn)[qr] = dsl;
+      }
     }
-    wait_vmem();
+    // the block's Q^T / dO^T operands: 4 steps of 32 queries, step (st, c) = queries
+    // Q0 + 64 st + 16 g + 8 c .. + 7 for lane group g (the rows the P / dS reads below take)
+    bf16x8 aq[4], ad[4];
+    __builtin_amdgcn_sched_barrier(0);  // not hoisted above the gradients (registers)
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int off = Q0 + 64 * (u >> 1) + 16 * g + 8 * (u & 1);
+      aq[u] = *(const bf16x8*)(qt_head + (row_off + off));
+      ad[u] = *(const bf16x8*)(dot_head + (row_off + off));
+    }
     __syncthreads();
-    // dV^T += dO^T P and dK^T += Q^T dS over the tile's 128 queries (4 steps of 32)
+    // dV^T += dO^T P and dK^T += Q^T dS over the block's 128 queries (4 steps of 32)
 #pragma unroll
-    for (int st = 0; st < 2; ++st) {
+    for (int u = 0; u < 4; ++u) {
+      const int st = u >> 1, c = u & 1;
+      // the read bases formed here, from opaque copies (hoisted out of the loop they stayed live
+      // across the gradients: 16 registers, spilled)
+      int vb[2] = {vbase[0], vbase[1]};
+      asm volatile("" : "+v"(vb[0]), "+v"(vb[1]));
+      int pbase[2][4];
+      ptr_bases(vb, pbase);
 #pragma unroll
-      for (int c = 0; c < 2; ++c) {
-        bf16x8 aq[MPW], ad[MPW];
-#pragma unroll
-        for (int a = 0; a < MPW; ++a) {
-          aq[a] = tr_read(lds + OFF_Q + st * TILE, vbase, c, mb0 + a);
-          ad[a] = tr_read(lds + OFF_DO + st * TILE, vbase, c, mb0 + a);
-        }
-#pragma unroll
-        for (int i = 0; i < KPW; ++i) {
-          const bf16x8 bs = ptr_read(lds + OFF_DS + st * (PT / 2), pbase, c, kc0 + i);
-          const bf16x8 bp = ptr_read(lds + OFF_P + st * (PT / 2), pbase, c, kc0 + i);
-#pragma unroll
-          for (int a = 0; a < MPW; ++a) {
-            dK[a][i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aq[a], bs, dK[a][i], 0, 0, 0);
-            dV[a][i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ad[a], bp, dV[a][i], 0, 0, 0);
-          }
-        }
+      for (int i = 0; i < KPW; ++i) {
+        const bf16x8 bs = ptr_read(lds + OFF_DS + st * (PT / 2), pbase, c, kc0 + i);
+        const bf16x8 bp = ptr_read(lds + OFF_P + st * (PT / 2), pbase, c, kc0 + i);
+        dK[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aq[u], bs, dK[i], 0, 0, 0);
+        dV[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ad[u], bp, dV[i], 0, 0, 0);
       }
     }
     __syncthreads();
@@ -872,18 +929,15 @@ __global__ void __launch_bounds__(512, 2) bwd_dkdv_kernel(BwdParams p) {
 
   // lane (n, g) holds dK^T[16 mb + 4g + r][key 16 kc + n]
 #pragma unroll
-  for (int a = 0; a < MPW; ++a) {
-#pragma unroll
-    for (int i = 0; i < KPW; ++i) {
-      const int row = J + 16 * (kc0 + i) + n;
-      if (row < Tn) {
-        const int d0 = 16 * (mb0 + a) + 4 * g;
-        bf16* ok = (bf16*)p.dk + head + (size_t)row * D + d0;
-        bf16* ov = (bf16*)p.dv + head + (size_t)row * D + d0;
-        const f32x4 k4 = dK[a][i], v4 = dV[a][i];
-        *(bf16x4*)ok = bf16x4{(bf16)k4[0], (bf16)k4[1], (bf16)k4[2], (bf16)k4[3]};
-        *(bf16x4*)ov = bf16x4{(bf16)v4[0], (bf16)v4[1], (bf16)v4[2], (bf16)v4[3]};
-      }
+  for (int i = 0; i < KPW; ++i) {
+    const int row = J + 16 * (kc0 + i) + n;
+    if (row < Tn) {
+      const int d0 = 16 * mb + 4 * g;
+      bf16* ok = (bf16*)p.dk + head + (size_t)row * D + d0;
+      bf16* ov = (bf16*)p.dv + head + (size_t)row * D + d0;
+      const f32x4 k4 = dK[i], v4 = dV[i];
+      *(bf16x4*)ok = bf16x4{(bf16)k4[0], (bf16)k4[1], (bf16)k4[2], (bf16)k4[3]};
+      *(bf16x4*)ov = bf16x4{(bf16)v4[0], (bf16)v4[1], (bf16)v4[2], (bf16)v4[3]};
     }
   }
 }
@@ -901,6 +955,8 @@ inline hipError_t launch_backward(const BwdParams& prm_in, hipStream_t stream) {
   prm.h0 = 0;
   prm.nh = BH;
   hipLaunchKernelGGL((bwd_pre_kernel<D>), dim3((unsigned)((rows + rpb - 1) / rpb)), dim3(256), 0, stream, prm);
+  hipLaunchKernelGGL((bwd_transpose_kernel<D>), dim3((unsigned)(BH * (bwd_tp(prm.T) / 64) * 2)), dim3(256), 0, stream,
+                     prm);
   const int nqb = (prm.T + kBlockRows - 1) / kBlockRows;
   const int nkb = (prm.T + kTile - 1) / kTile;
   auto sink = [&]() {

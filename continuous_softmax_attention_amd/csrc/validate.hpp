@@ -128,7 +128,9 @@ inline int64_t backward_workspace_bytes(int64_t B, int64_t H, int64_t T, int64_t
   if (d != 64 && d != 128) return -1;
   const int64_t kMax32 = (int64_t(1) << 31) - 1;
   if (T > kMax32 / 2 || B > kMax32 || H > kMax32 || B * H > kMax32 / T) return -1;  // B*H*T rows < 2^31
-  return 512 + 16 * B * H * T + B * H * 16 * 2 * 128 * 4;  // see bwd16.hpp for the layout
+  const int64_t tp = (T + 127) / 128 * 128;
+  const int64_t head = (512 + 16 * B * H * T + B * H * 16 * 2 * 128 * 4 + 255) / 256 * 256;
+  return head + 2 * B * H * d * tp * 2;  // see bwd16.hpp for the layout
 }
 
 // Optional last region of the backward workspace: the bf16 dS tiles that let dq be a plain

@@ -225,7 +225,8 @@ int csa_decode_noalloc_check(const void* q, const void* k, const void* v, const 
  *   dk0, dv0   device, [B, H, d] bf16 outputs (16-byte aligned), or NULL to skip; written even
  *              when k0 / v0 is NULL (the gradient at the zero vector).
  *   workspace  device, 16-byte aligned, at least csa_backward_workspace_bytes(B, H, T, d)
- *              bytes, caller-owned scratch (no initialisation needed); calls sharing it must be
+ *              bytes (row statistics and transposed copies of q and dout: about 4*B*H*T*d
+ *              bytes), caller-owned scratch (no initialisation needed); calls sharing it must be
  *              ordered on one stream.  With at least csa_backward_workspace_bytes_kept(B, H, T,
  *              d, 1) bytes the call also keeps dS (bf16, about T*T bytes per head) so that it is
  *              computed once instead of twice: for as many heads at a time as the workspace

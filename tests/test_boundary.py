@@ -282,9 +282,14 @@ def _bcheck(**kw):
 
 def test_backward_workspace_size():
     # 512 zero bytes, then D_t, mu_t, dS_{t,0}, P_{t,0} as float32 per (b, h, t), then
-    # 16 partial sums of dk_0 and dv_0 (2 x 128 float32) per (b, h)
-    assert csa.csa_backward_workspace_bytes(2, 3, 100, 64) == 512 + 16 * 2 * 3 * 100 + 2 * 3 * 16 * 1024
-    assert csa.csa_backward_workspace_bytes(4, 16, 4096, 128) == 512 + 16 * 4 * 16 * 4096 + 64 * 16 * 1024
+    # 16 partial sums of dk_0 and dv_0 (2 x 128 float32) per (b, h); then, 256-byte aligned,
+    # Q^T and dO^T per (b, h) as d rows of T rounded up to 128 bf16
+    def expect(B, H, T, d):
+        head = 512 + 16 * B * H * T + B * H * 16 * 1024
+        return (head + 255) // 256 * 256 + 2 * B * H * d * ((T + 127) // 128 * 128) * 2
+    assert csa.csa_backward_workspace_bytes(2, 3, 100, 64) == expect(2, 3, 100, 64)
+    assert csa.csa_backward_workspace_bytes(4, 16, 4096, 128) == expect(4, 16, 4096, 128)
+    assert expect(4, 16, 4096, 128) - 2 * 4 * 16 * 4096 * 128 * 2 < 6 << 20  # the rest is O(B H T)
     for bad in (dict(d=16), dict(d=32), dict(B=0), dict(T=0), dict(H=-1)):
         a = dict(B=1, H=1, T=100, d=64)
         a.update(bad)

@@ -299,8 +299,20 @@ __global__ void __launch_bounds__(512, 4) attn16_kernel(FwdParams p) {
   auto from_lane = [&](int src, float x) {  // value of x in lane src
     return __int_as_float(__builtin_amdgcn_ds_bpermute(src << 2, __float_as_int(x)));
   };
-  const int lane_dn = (lane + 16) & 63;  // same query, next lane group
-  const int lane_up = (lane - 16) & 63;  // same query, previous lane group
+  // lanes of the same query in the next / previous lane group, formed where used from the
+  // lane index (kept live across the tile loop they were spilled to scratch)
+  auto lane_dn = [&]() {
+    const int l = (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+    int r = (l + 16) & 63;
+    asm volatile("" : "+v"(r));
+    return r;
+  };
+  auto lane_up = [&]() {
+    const int l = (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+    int r = (l + 48) & 63;
+    asm volatile("" : "+v"(r));
+    return r;
+  };
 
   // ---- logit of position 0: a0 = q . k0 (zero when k0 is null)
   float a0 = 0.0f;
@@ -519,8 +531,8 @@ __global__ void __launch_bounds__(512, 4) attn16_kernel(FwdParams p) {
       // the previous tile's key 63 carried by lanes g = 3, or (first tile) position 0;
       // right of key 15 is the next group's key 0, or (g = 3) the halo
       const float lsend = g == 3 ? carry_s : s[15];
-      float left = from_lane(lane_up, lsend);
-      float right = from_lane(lane_dn, s[0]);
+      float left = from_lane(lane_up(), lsend);
+      float right = from_lane(lane_dn(), s[0]);
       carry_s = s[15];
       if (first && g == 0) left = a0;
       if (!last && g == 3) right = halo;
@@ -550,8 +562,8 @@ __global__ void __launch_bounds__(512, 4) attn16_kernel(FwdParams p) {
       const float al15 = alpha(15);
       const float pv15 = exp2_fast(al15);
       // right neighbour of key 15: the next group's key 0, or (g = 3) the halo
-      float ar = from_lane(lane_dn, al0);
-      float pr = from_lane(lane_dn, pv0);
+      float ar = from_lane(lane_dn(), al0);
+      float pr = from_lane(lane_dn(), pv0);
       if (!last) {
         const float ah = __builtin_fmaf(halo, kLog2e, -mr);
         if (g == 3) {
@@ -564,7 +576,7 @@ __global__ void __launch_bounds__(512, 4) attn16_kernel(FwdParams p) {
       // left term of key 0: from the previous group, or (g = 0) carried from the
       // previous tile's group 3, or (first tile) from the edge with position 0
       const float Lsend = g == 3 ? carry : Lnext;
-      float Lprev = from_lane(lane_up, Lsend);
+      float Lprev = from_lane(lane_up(), Lsend);
       carry = Lnext;  // lanes g = 3: left term of key 64(j+1)
       if (first) {    // position 0: only its right neighbour (eq. (10), i = 0)
         const float a0l = __builtin_fmaf(a0, kLog2e, -mr);

@@ -383,9 +383,9 @@ def csa_decode_noalloc(q, k, v, k0=None, v0=None, *, out=None, lse=None, return_
 
 def csa_backward(q, k, v, o, lse, dout, k0=None, v0=None, *, sink_grads=True, dq=None, dk=None, dv=None,
                  workspace=None, stream=None):
-    """Gradients of the causal CSA forward through libcsa (bfloat16, d in {64, 128}).
+    """Gradients of the causal CSA forward through libcsa (bfloat16 or float32, d in {16, 64, 128}).
 
-    q, k, v, o (the forward's output), dout: [B, H, T, d] bfloat16 device tensors; lse: the
+    q, k, v, o (the forward's output), dout: [B, H, T, d] device tensors of one dtype; lse: the
     forward's [B, H, T] float32 lse; k0, v0: [B, H, d] or None (zeros).  Returns
     (dq, dk, dv, dk0, dv0) -- dk0 and dv0 ([B, H, d]) are None when sink_grads is False.
     ``workspace``: a device tensor of at least csa_backward_workspace_bytes(B, H, T, d) bytes;
@@ -409,14 +409,14 @@ def csa_backward(q, k, v, o, lse, dout, k0=None, v0=None, *, sink_grads=True, dq
             _check(name, t, (B, H, d), dt, dev)
     need = csa_backward_workspace_bytes(B, H, T, d)
     if need < 0:
-        raise CsaError(CSA_ERR_UNSUPPORTED if d not in (64, 128) else CSA_ERR_INVALID_ARG, "csa_backward (sizes)")
+        raise CsaError(CSA_ERR_UNSUPPORTED if d not in (16, 64, 128) else CSA_ERR_INVALID_ARG, "csa_backward (sizes)")
     if workspace is None:
         # dS kept for as many heads at a time as fit min(2 GiB, a quarter of the free device
         # memory) -- it grows as T^2 per head -- else the O(B H T) workspace (dS recomputed);
         # the results are identical either way
         free, _ = torch.cuda.mem_get_info(dev)
         budget = min(KEPT_DS_BUDGET_BYTES, free // 4)
-        one = csa_backward_workspace_bytes_kept(B, H, T, d, 1)
+        one = csa_backward_workspace_bytes_kept(B, H, T, d, 1) if dt == torch.bfloat16 else -1
         size = need
         if 0 < one <= budget:
             per_head = csa_backward_workspace_bytes_kept(B, H, T, d, 2) - one if B * H > 1 else 0

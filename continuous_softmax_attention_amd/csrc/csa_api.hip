@@ -7,6 +7,7 @@
 
 #include "attn16.hpp"
 #include "bwd16.hpp"
+#include "bwdv.hpp"
 #include "dec16.hpp"
 #include "decode.hpp"
 #include "attn_fwd.hpp"
@@ -237,11 +238,20 @@ extern "C" int csa_backward(const void* q, const void* k, const void* v, const v
   if (st != CSA_OK) return st;
   // dS kept for as many heads at a time as the workspace holds (the kernels run on groups of
   // that many heads), else recomputed
-  const int64_t kept = csa::backward_kept_heads(B, H, T, d, workspace_bytes);
+  const int64_t kept = csa::backward_kept_heads_for(B, H, T, d, dtype, workspace_bytes);
   char* ds = kept > 0 ? (char*)workspace + csa::backward_ds_offset(B, H, T, d) : nullptr;
   csa::BwdParams p{q, k, v, k0, v0, o, lse, dout, dq, dk, dv, dk0, dv0, (char*)workspace,
                    (int)B, (int)H, (int)T, ds, csa::backward_ds_tiles_per_head(T), 0, (int)kept};
-  const hipError_t e = d == 64 ? csa::launch_backward<64>(p, (hipStream_t)stream)
-                               : csa::launch_backward<128>(p, (hipStream_t)stream);
+  const hipStream_t s = (hipStream_t)stream;
+  hipError_t e;
+  if (dtype == CSA_F32) {  // float32: the VALU kernels (bwdv.hpp)
+    e = d == 16 ? csa::launch_backward_valu<float, 16>(p, s)
+        : d == 64 ? csa::launch_backward_valu<float, 64>(p, s)
+                  : csa::launch_backward_valu<float, 128>(p, s);
+  } else if (d == 16) {
+    e = csa::launch_backward_valu<csa::bf16, 16>(p, s);
+  } else {
+    e = d == 64 ? csa::launch_backward<64>(p, s) : csa::launch_backward<128>(p, s);
+  }
   return e == hipSuccess ? CSA_OK : CSA_ERR_HIP;
 }

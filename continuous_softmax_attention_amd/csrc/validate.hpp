@@ -125,7 +125,7 @@ inline int validate_decode_noalloc(const void* q, const void* k, const void* v, 
 // overlap another output or any input.
 inline int64_t backward_workspace_bytes(int64_t B, int64_t H, int64_t T, int64_t d) {
   if (B < 1 || H < 1 || T < 1) return -1;
-  if (d != 64 && d != 128) return -1;
+  if (d != 16 && d != 64 && d != 128) return -1;
   const int64_t kMax32 = (int64_t(1) << 31) - 1;
   if (T > kMax32 / 2 || B > kMax32 || H > kMax32 || B * H > kMax32 / T) return -1;  // B*H*T rows < 2^31
   const int64_t tp = (T + 127) / 128 * 128;
@@ -149,6 +149,7 @@ inline int64_t backward_ds_offset(int64_t B, int64_t H, int64_t T, int64_t d) {
 // Workspace with which the dS tiles of `heads` heads at a time are kept (1 <= heads <= B*H;
 // the kernels then run on groups of that many heads), or -1.
 inline int64_t backward_workspace_bytes_kept(int64_t B, int64_t H, int64_t T, int64_t d, int64_t heads) {
+  if (d != 64 && d != 128) return -1;  // the kept-dS path: bf16 at d = 64, 128
   const int64_t off = backward_ds_offset(B, H, T, d);
   if (off < 0 || heads < 1 || heads > B * H) return -1;
   const int64_t tiles = backward_ds_tiles_per_head(T);
@@ -160,6 +161,7 @@ inline int64_t backward_workspace_bytes_fast(int64_t B, int64_t H, int64_t T, in
   return backward_workspace_bytes_kept(B, H, T, d, B * H);
 }
 // Heads whose dS tiles fit a workspace of ws_bytes (0: the recompute path), at most B*H.
+// (backward_kept_heads_for: 0 also for the float32 and d = 16 kernels, which keep no dS.)
 inline int64_t backward_kept_heads(int64_t B, int64_t H, int64_t T, int64_t d, int64_t ws_bytes) {
   const int64_t one = backward_workspace_bytes_kept(B, H, T, d, 1);
   if (one < 0 || ws_bytes < one) return 0;
@@ -168,23 +170,28 @@ inline int64_t backward_kept_heads(int64_t B, int64_t H, int64_t T, int64_t d, i
   return g < B * H ? g : B * H;
 }
 
+inline int64_t backward_kept_heads_for(int64_t B, int64_t H, int64_t T, int64_t d, int dtype, int64_t ws_bytes) {
+  return dtype == CSA_BF16 && d != 16 ? backward_kept_heads(B, H, T, d, ws_bytes) : 0;
+}
+
 inline int validate_backward(const void* q, const void* k, const void* v, const void* k0, const void* v0,
                              const void* o, const float* lse, const void* dout, const void* dq, const void* dk,
                              const void* dv, const void* dk0, const void* dv0, const void* ws, int64_t ws_bytes,
                              int64_t B, int64_t H, int64_t T, int64_t d, int dtype) {
-  if (dtype != CSA_BF16) return CSA_ERR_UNSUPPORTED;
-  if (d != 64 && d != 128) return CSA_ERR_UNSUPPORTED;
+  if (dtype != CSA_BF16 && dtype != CSA_F32) return CSA_ERR_UNSUPPORTED;
+  if (d != 16 && d != 64 && d != 128) return CSA_ERR_UNSUPPORTED;
   if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv || !ws) return CSA_ERR_INVALID_ARG;
   const int64_t need_min = backward_workspace_bytes(B, H, T, d);
   if (need_min < 0 || ws_bytes < need_min) return CSA_ERR_INVALID_ARG;
-  const int64_t kept = backward_kept_heads(B, H, T, d, ws_bytes);
+  const int64_t kept = backward_kept_heads_for(B, H, T, d, dtype, ws_bytes);
   const int64_t need = kept > 0 ? backward_workspace_bytes_kept(B, H, T, d, kept) : need_min;  // the part used
   for (const void* p : {q, k, v, o, dout, dq, dk, dv, ws})
     if (!aligned(p, 16)) return CSA_ERR_INVALID_ARG;
   for (const void* p : {k0, v0, dk0, dv0})
     if (p && !aligned(p, 16)) return CSA_ERR_INVALID_ARG;
   if (!aligned(lse, 4)) return CSA_ERR_INVALID_ARG;
-  const int64_t big = B * H * T * d * 2, small = B * H * d * 2;
+  const int64_t esize = dtype == CSA_F32 ? 4 : 2;
+  const int64_t big = B * H * T * d * esize, small = B * H * d * esize;
   const Span ins[8] = {span_of(q, big),  span_of(k, big),  span_of(v, big),  span_of(k0, small),
                        span_of(v0, small), span_of(o, big), span_of(lse, B * H * T * 4), span_of(dout, big)};
   const Span outs[6] = {span_of(dq, big),    span_of(dk, big),    span_of(dv, big),

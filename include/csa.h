@@ -216,13 +216,13 @@ int csa_decode_noalloc_check(const void* q, const void* k, const void* v, const 
  * with P_{t,i} = e^{a_{t,i} + b_{t,i}} / Z_t, edges only between consecutive positions 0..t,
  * and dq_t = sum_i dS_{t,i} k_i, dk_i = sum_t dS_{t,i} q_t, dv_i = sum_t P_{t,i} dO_t.
  *
- *   q, k, v    device, [B, H, T, d] bf16, 16-byte aligned (the forward's inputs).
- *   k0, v0     device, [B, H, d] bf16, 16-byte aligned, or NULL (zeros), as in csa_forward.
- *   o, lse     device: the forward's out [B, H, T, d] bf16 and lse [B, H, T] float32 (4-byte
+ *   q, k, v    device, [B, H, T, d] `dtype`, 16-byte aligned (the forward's inputs).
+ *   k0, v0     device, [B, H, d] `dtype`, 16-byte aligned, or NULL (zeros), as in csa_forward.
+ *   o, lse     device: the forward's out [B, H, T, d] `dtype` and lse [B, H, T] float32 (4-byte
  *              aligned) for these inputs; P is recomputed from lse.
- *   dout       device, [B, H, T, d] bf16: dLoss/do.
- *   dq, dk, dv device, [B, H, T, d] bf16 outputs (fully written).
- *   dk0, dv0   device, [B, H, d] bf16 outputs (16-byte aligned), or NULL to skip; written even
+ *   dout       device, [B, H, T, d] `dtype`: dLoss/do.
+ *   dq, dk, dv device, [B, H, T, d] `dtype` outputs (fully written).
+ *   dk0, dv0   device, [B, H, d] `dtype` outputs (16-byte aligned), or NULL to skip; written even
  *              when k0 / v0 is NULL (the gradient at the zero vector).
  *   workspace  device, 16-byte aligned, at least csa_backward_workspace_bytes(B, H, T, d)
  *              bytes (row statistics and transposed copies of q and dout: about 4*B*H*T*d
@@ -233,11 +233,14 @@ int csa_decode_noalloc_check(const void* q, const void* k, const void* v, const 
  *              holds (all B*H with csa_backward_workspace_bytes_fast bytes), the dk/dv and dq
  *              kernels running on one group of heads after another.  The results are bitwise
  *              identical whichever path and group size the workspace selects.
- *   d          64 or 128 (16 returns CSA_ERR_UNSUPPORTED); dtype must be CSA_BF16.
+ *   d          16, 64 or 128.  dtype CSA_BF16 or CSA_F32.
  *   stream     hipStream_t or NULL.
  *
- * Gradients are accumulated in float32 and rounded once to bf16; the bf16 operands of the
- * matrix products (P, dS) are rounded like the forward's P.  Returns CSA_OK, or
+ * bf16 at d = 64, 128: the matrix-core kernels; gradients are accumulated in float32 and
+ * rounded once to bf16, and the bf16 operands of the matrix products (P, dS) are rounded like
+ * the forward's P.  float32 (any d) and bf16 at d = 16: VALU kernels in float32 throughout
+ * (no rounding of P or dS; outputs rounded once to the dtype); the kept-dS workspace does not
+ * apply to them.  Returns CSA_OK, or
  * CSA_ERR_INVALID_ARG (null required pointer, sizes, alignment, a short workspace, or any
  * output overlapping another output or an input), CSA_ERR_UNSUPPORTED, CSA_ERR_HIP; nothing is
  * launched on an error.  Up to five kernel launches on `stream`.

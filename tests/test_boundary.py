@@ -290,7 +290,8 @@ def test_backward_workspace_size():
     assert csa.csa_backward_workspace_bytes(2, 3, 100, 64) == expect(2, 3, 100, 64)
     assert csa.csa_backward_workspace_bytes(4, 16, 4096, 128) == expect(4, 16, 4096, 128)
     assert expect(4, 16, 4096, 128) - 2 * 4 * 16 * 4096 * 128 * 2 < 6 << 20  # the rest is O(B H T)
-    for bad in (dict(d=16), dict(d=32), dict(B=0), dict(T=0), dict(H=-1)):
+    assert csa.csa_backward_workspace_bytes(1, 2, 100, 16) == expect(1, 2, 100, 16)
+    for bad in (dict(d=32), dict(d=96), dict(B=0), dict(T=0), dict(H=-1)):
         a = dict(B=1, H=1, T=100, d=64)
         a.update(bad)
         assert csa.csa_backward_workspace_bytes(a["B"], a["H"], a["T"], a["d"]) == -1
@@ -325,9 +326,12 @@ def test_backward_check_rules():
     assert _bcheck(d=128) == OK
     assert _bcheck(dk0=None, dv0=None) == OK
     assert _bcheck(k0=A + 12 * MB, v0=A + 13 * MB) == OK
-    assert _bcheck(dtype=csa.CSA_F32) == UNS   # bf16 kernels only
-    assert _bcheck(d=16) == UNS
+    assert _bcheck(dtype=csa.CSA_F32) == OK    # float32: the VALU kernels
+    assert _bcheck(d=16) == OK                 # bf16 at d = 16: the VALU kernels
+    assert _bcheck(d=16, dtype=csa.CSA_F32) == OK
+    assert _bcheck(d=32) == UNS
     assert _bcheck(d=96) == UNS
+    assert _bcheck(dtype=7) == UNS
     for field in ("q", "k", "v", "o", "lse", "dout", "dq", "dk", "dv", "ws"):
         assert _bcheck(**{field: None}) == INV, field
     for bad in (dict(wsb=512 + 16 * 600 + 6 * 16 * 1024 - 1),   # one byte short
@@ -341,10 +345,11 @@ def test_backward_check_rules():
                 dict(dk0=A + 4 * MB)):                    # dk0 inside lse
         assert _bcheck(**bad) == INV, bad
     # the launching entry point rejects the same calls before any HIP call
-    a = _bargs(dtype=csa.CSA_F32)
-    assert csa.csa_backward_raw(a["q"], a["k"], a["v"], None, None, a["o"], a["lse"], a["dout"], a["dq"], a["dk"],
-                                a["dv"], None, None, a["ws"], a["wsb"], a["B"], a["H"], a["T"], a["d"],
-                                a["dtype"]) == UNS
+    for bad, code in ((dict(d=32), UNS), (dict(dtype=7), UNS), (dict(q=A + 8), INV)):
+        a = _bargs(**bad)
+        assert csa.csa_backward_raw(a["q"], a["k"], a["v"], None, None, a["o"], a["lse"], a["dout"], a["dq"], a["dk"],
+                                    a["dv"], None, None, a["ws"], a["wsb"], a["B"], a["H"], a["T"], a["d"],
+                                    a["dtype"]) == code, bad
 
 
 def test_status_strings():

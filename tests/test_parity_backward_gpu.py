@@ -227,15 +227,93 @@ def test_long_workload_full_size():
 
 
 def test_rejects_unsupported_before_launch():
-    q = torch.zeros(1, 1, 8, 64, device=DEV)
     lse = torch.zeros(1, 1, 8, device=DEV)
-    with pytest.raises(csa.CsaError) as e:  # float32: the backward kernels are bf16
-        csa.csa_backward(q, q, q, q, lse, q)
-    assert e.value.status == csa.CSA_ERR_UNSUPPORTED
-    qb = torch.zeros(1, 1, 8, 16, device=DEV, dtype=torch.bfloat16)
-    with pytest.raises(csa.CsaError) as e:
-        csa.csa_backward(qb, qb, qb, qb, lse, qb)
-    assert e.value.status == csa.CSA_ERR_UNSUPPORTED
+    for dt in (torch.float32, torch.bfloat16):
+        q = torch.zeros(1, 1, 8, 32, device=DEV, dtype=dt)  # d = 32: no kernel
+        with pytest.raises(csa.CsaError) as e:
+            csa.csa_backward(q, q, q, q, lse, q)
+        assert e.value.status == csa.CSA_ERR_UNSUPPORTED
+
+
+# ---------------------------------------------------------------- float32, and bf16 at d = 16
+# (the VALU kernels of bwdv.hpp: float32 arithmetic throughout, no bf16 rounding of P or dS).
+# float32 bar: max |G - G_ref| <= 1e-5 * max(1, max |G_ref|), the forward's float32 bar on the
+# gradient scaled to unit size; at logit std 8 the forward's float32 bar is 4e-5 (float32
+# logits of size ~40 carry ~|a| 2^-24 rounding each), and so is this one.
+TOL32 = 1e-5
+
+
+def _random_case_dt(B, H, T, d, seed, dtype, q_mult=1.0, sink=True):
+    g = torch.Generator().manual_seed(seed)
+    q = torch.randn(B, H, T, d, generator=g) * (q_mult / math.sqrt(d))
+    k = torch.randn(B, H, T, d, generator=g)
+    v = torch.randn(B, H, T, d, generator=g)
+    k0 = torch.randn(B, H, d, generator=g) if sink else None
+    v0 = torch.randn(B, H, d, generator=g) if sink else None
+    cast = (lambda t: None if t is None else t.to(dtype))
+    do = make_grad_output((B, H, T, d), dtype, seed)
+    return cast(q), cast(k), cast(v), cast(k0), cast(v0), do
+
+
+def _compare_tol(tag, got, ref, tol):
+    errs = {}
+    for name, g, r in zip(NAMES, got, ref):
+        assert np.all(np.isfinite(g)), f"{tag}: non-finite {name}"
+        errs[name] = _nerr(g, r)
+    print(f"[parity backward] {tag}: " + "  ".join(f"{n} {e:.2e}" for n, e in errs.items()), flush=True)
+    for name, e in errs.items():
+        assert e <= tol, (tag, name, e)
+
+
+@pytest.mark.parametrize("name", ["tiny", "tile", "tail"])
+def test_f32_workloads_every_row(name):
+    q, k, v, k0, v0 = make_inputs(name)
+    do = make_grad_output(q.shape, q.dtype, 11)
+    got = _run(q, k, v, k0, v0, do)
+    ref = csa_backward_reference(q, k, v, do, k0, v0)
+    _compare_tol(f"f32 {name}", got, ref, TOL32)
+
+
+@pytest.mark.parametrize("d", [16, 64, 128])
+@pytest.mark.parametrize("T", [1, 2, 3, 61, 62, 63, 64, 124, 125, 200])
+def test_f32_edge_shapes_random_sink(T, d):
+    q, k, v, k0, v0, do = _random_case_dt(1, 2, T, d, seed=5000 + T + d, dtype=torch.float32)
+    got = _run(q, k, v, k0, v0, do)
+    _compare_tol(f"f32 T{T} d{d}", got, csa_backward_reference(q, k, v, do, k0, v0), TOL32)
+
+
+def test_f32_large_logits_copied_sink():
+    q, k, v, _, _, do = _random_case_dt(1, 2, 300, 64, seed=71, dtype=torch.float32, q_mult=8.0, sink=False)
+    k0, v0 = k[:, :, 0].clone(), v[:, :, 0].clone()  # copied sink: an exactly zero first difference
+    got = _run(q, k, v, k0, v0, do)
+    _compare_tol("f32 logit std 8, copied sink", got, csa_backward_reference(q, k, v, do, k0, v0), 4 * TOL32)
+
+
+@pytest.mark.parametrize("T", [1, 2, 65, 200, 513])
+def test_bf16_d16(T):
+    q, k, v, k0, v0, do = _random_case_dt(2, 3, T, 16, seed=6000 + T, dtype=torch.bfloat16)
+    got = _run(q, k, v, k0, v0, do)
+    _compare_tol(f"bf16 d16 T{T}", got, csa_backward_reference(q, k, v, do, k0, v0), TOL)
+
+
+def test_f32_shift_symmetries_and_equal_logits():
+    # q = 0: every logit equal, so P is the trapezoid weights (1/2, 1, ..., 1, 1/2)/t and
+    # dv_i = sum_t P_{t,i} dO_t exactly; the value- and key-shift symmetries hold for any input
+    T, d = 150, 64
+    _, k, v, k0, v0, do = _random_case_dt(1, 1, T, d, seed=81, dtype=torch.float32)
+    q = torch.zeros(1, 1, T, d)
+    dq, dk, dv, dk0, dv0 = _run(q, k, v, k0, v0, do)
+    dov = do[0, 0].double().numpy()
+    want = np.zeros((T + 1, d))
+    for t in range(1, T + 1):
+        w = np.ones(t + 1)
+        w[0] = w[t] = 0.5
+        want[: t + 1] += np.outer(w / t, dov[t - 1])
+    got = np.concatenate([dv0[0, 0][None], dv[0, 0]])
+    assert np.abs(got - want).max() <= TOL32 * max(1.0, np.abs(want).max())
+    # sum over positions of dv = sum_t dO_t; sum over positions of dk = 0 (no lse gradient)
+    assert np.abs(got.sum(0) - dov.sum(0)).max() <= 1e-4
+    assert np.abs(dk[0, 0].sum(0) + dk0[0, 0]).max() <= 1e-4 * max(1.0, np.abs(dk).max())
 
 
 def _check_shift_symmetries(tag, do, got):

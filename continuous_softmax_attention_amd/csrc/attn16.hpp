@@ -180,6 +180,15 @@ __device__ __forceinline__ void upper_half(float al, float pl, float ar, float p
 
 }  // namespace half
 
+// The lane index, produced where it is used: an instruction pair the compiler can neither
+// hoist nor merge, so that values derived from the lane index are formed anew at each use
+// instead of being kept in registers across the tile loop.
+__device__ inline int lane_here() {
+  int l;
+  asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(l));
+  return l;
+}
+
 // kHalf differs from kExact in two places only: position 0 and position 1 share the upper
 // half of segment (0, 1) (first tile), and the query's own position t and position t+1 share
 // the lower half of segment (t, t+1) -- all of it, c^2 p_t / 2, to position t for the last
@@ -202,6 +211,16 @@ __global__ void __launch_bounds__(512, 4) attn16_kernel(FwdParams p) {
   constexpr int REGION = 64 * RW * 16;           // bytes per region
 
   __shared__ __attribute__((aligned(1024))) char smem[4 * TILE_BYTES];  // K0 K1 V0 V1
+  // Per query of the block, values used only outside the steady tile loop, kept here instead
+  // of in registers across it (with them in registers the d = 128 kernels spilled 6 to 25
+  // VGPRs to scratch at 128 VGPRs): slot 0 a0, 1 a_t, 2 a_t1 (interval variant), 3 the HL
+  // of position t + 1 when it opens the next tile (interval variant), 4 the weight of
+  // position 0 (rescaled in place when the shift moves).  Each wave owns its 16 queries'
+  // slots, so no barrier is involved; a wave's LDS accesses complete in order.
+  __shared__ float parked[kWaves16 * 16 * 8];
+  // interval variant: the value row of position t + 1 of a wave's last query when it opens
+  // the next tile (its weight is added in the epilogue), loaded in the prologue
+  __shared__ bf16 vnext[W == kHalf ? kWaves16 * D : 1];
   CSA_LDS char* lds = (CSA_LDS char*)smem;
 
   const int tid = threadIdx.x;
@@ -265,6 +284,13 @@ __global__ void __launch_bounds__(512, 4) attn16_kernel(FwdParams p) {
     }
   };
 
+  // ---- prologue copies first, K_0, V_0, K_1 into LDS: the loads of Q, k0 and (interval
+  // variant) of the key and value rows below are then in flight together with them, and
+  // the whole prologue waits for one round trip to memory instead of two or three
+  stage(0, Kg, 0, false);
+  stage(2, Vg, 0, true);
+  if (jmax >= 1) stage(1, Kg, 1, false);
+
   // ---- Q operand in registers: qreg[s] = chunk 4s + g of row qr (zero past d)
   bf16x8 qreg[NSTEP];
   {
@@ -314,6 +340,38 @@ __global__ void __launch_bounds__(512, 4) attn16_kernel(FwdParams p) {
     return r;
   };
 
+  // this lane's query slot k of `parked`, addressed from the lane index where used
+  auto park = [&](int k) -> CSA_LDS float* {
+    const int off = (16 * wave + (lane_here() & 15)) * 32 + 4 * k;
+    return (CSA_LDS float*)((CSA_LDS char*)parked + off);
+  };
+
+  // this lane's query row, formed from the lane index where used (not kept across the loop)
+  auto qrow = [&]() { return qw + (lane_here() & 15); };
+
+  // interval variant: key rows qr (position t) and qr + 1 (position t + 1), whose logits
+  // the lower half of segment (t, t+1) on the diagonal tile needs; loaded before the k0 row
+  // so that all of the prologue's loads are in flight at once
+  bf16x8 kt[W == kHalf ? NSTEP : 1], kn[W == kHalf ? NSTEP : 1];
+  // and, when the wave's last query's position t + 1 opens the next tile (wave-uniform), the
+  // value row of that position, one 4-byte piece per lane, for `vnext`
+  const bool vrow_wave = W == kHalf && ((qw + 15) & 63) == 63;
+  unsigned vpiece = 0;
+  if (vrow_wave && lane_here() < D / 2)
+    vpiece = *(const unsigned*)((const bf16*)p.v + head + (size_t)min(qw + 16, Tn - 1) * D +
+                                2 * lane_here());
+  if constexpr (W == kHalf) {
+    const bf16* Kh = (const bf16*)p.k + head;
+    const int rt = min(qr, Tn - 1), rn = min(qr + 1, Tn - 1);
+#pragma unroll
+    for (int s = 0; s < NSTEP; ++s) {
+      if (4 * s + g < CH) {
+        kt[s] = *(const bf16x8*)(Kh + (size_t)rt * D + (4 * s + g) * 8);
+        kn[s] = *(const bf16x8*)(Kh + (size_t)rn * D + (4 * s + g) * 8);
+      }
+    }
+  }
+
   // ---- logit of position 0: a0 = q . k0 (zero when k0 is null)
   float a0 = 0.0f;
   if (CSA && p.k0 != nullptr) {
@@ -329,31 +387,27 @@ __global__ void __launch_bounds__(512, 4) attn16_kernel(FwdParams p) {
     }
     a0 = qsum(part);
   }
-  // interval variant: logits of key rows qr (position t) and qr + 1 (position t + 1), for the
-  // lower half of segment (t, t+1) on the diagonal tile; loaded here, in the shadow of the
-  // first tile's copies
+  if (CSA) *park(0) = a0;
   float a_t = 0.0f, a_t1 = 0.0f;
-  const bool lastq = qr == Tn - 1;
   if constexpr (W == kHalf) {
-    const bf16* Kh = (const bf16*)p.k + head;
-    const int rt = min(qr, Tn - 1), rn = min(qr + 1, Tn - 1);
     float pt = 0.0f, pn = 0.0f;
 #pragma unroll
     for (int s = 0; s < NSTEP; ++s) {
       if (4 * s + g < CH) {
-        const bf16x8 kt = *(const bf16x8*)(Kh + (size_t)rt * D + (4 * s + g) * 8);
-        const bf16x8 kn = *(const bf16x8*)(Kh + (size_t)rn * D + (4 * s + g) * 8);
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          pt = __builtin_fmaf((float)qreg[s][e], (float)kt[e], pt);
-          pn = __builtin_fmaf((float)qreg[s][e], (float)kn[e], pn);
+          pt = __builtin_fmaf((float)qreg[s][e], (float)kt[s][e], pt);
+          pn = __builtin_fmaf((float)qreg[s][e], (float)kn[s][e], pn);
         }
       }
     }
     a_t = qsum(pt);
     a_t1 = qsum(pn);
+    *park(1) = a_t;
+    *park(2) = a_t1;
+    if (vrow_wave && lane_here() < D / 2)
+      *(CSA_LDS unsigned*)((CSA_LDS char*)vnext + 2 * D * wave + 4 * lane_here()) = vpiece;
   }
-  float hl_next = 0.0f;  // interval variant: HL when position t + 1 is the next tile's first key
 
   // ---- LDS read bases
   // K operand (block b, step s): row 16(n >> 2) + 4b + (n & 3), chunk 4s + g (for d = 16,
@@ -403,14 +457,14 @@ __global__ void __launch_bounds__(512, 4) attn16_kernel(FwdParams p) {
   float m_run = -__builtin_inff();
   float carry = 0.0f;   // lanes g = 3: left term of the next tile's first key (exact rule)
   float carry_s = 0.0f; // logit of this lane's key 15 in the previous tile (first-order rule)
-  float w0 = 0.0f;      // lanes g = 0: weight of position 0
+  if (CSA) *park(4) = 0.0f;  // weight of position 0 (lanes g = 0 write it)
 
   auto rescale_all = [&](float sc) {
 #pragma unroll
     for (int mb = 0; mb < NMB; ++mb) O[mb] *= sc;
     lsum *= sc;
     carry *= sc;
-    w0 *= sc;
+    if (CSA && g == 0) *park(4) *= sc;
   };
 
   // ---------------------------------------------------------------- one tile
@@ -437,8 +491,12 @@ __global__ void __launch_bounds__(512, 4) attn16_kernel(FwdParams p) {
 #pragma unroll
     for (int t = 0; t < 16; ++t) s[t] = Scur[t >> 2][t & 3];
     // key row of s[t] is j*64 + 16g + t; visible to this lane's query iff t <= lim
-    int lim = qr - (j * kTile + 16 * g);
-    asm volatile("" : "+v"(lim));  // opaque: keeps "t <= lim" from becoming 16 constants
+    int lim = 0;
+    if constexpr (last) {
+      const int l = lane_here();
+      lim = qw + (l & 15) - (j * kTile + 16 * (l >> 4));
+      asm volatile("" : "+v"(lim));  // opaque: keeps "t <= lim" from becoming 16 constants
+    }
 
     // -- running maximum (lazy: the shift moves only when the maximum grows by > 2^8)
     float mx = -__builtin_inff();
@@ -454,8 +512,19 @@ __global__ void __launch_bounds__(512, 4) attn16_kernel(FwdParams p) {
       halo = from_lane(n, Snext[0][0]);  // key 0 of tile j+1 (lane n, g = 0)
       mx = fmaxf(mx, halo);
     }
-    if (CSA && first) mx = fmaxf(mx, a0);
-    if (W == kHalf && last && !lastq) mx = fmaxf(mx, a_t1);  // position t + 1 takes a weight
+    // a0: in a register for the peeled first tile, from `parked` for a diagonal tile 0
+    float a0v = 0.0f;
+    if constexpr (CSA) {
+      if constexpr (decltype(first_c)::value) a0v = a0;
+      else if (first) a0v = *park(0);
+    }
+    float a_tv = 0.0f, a_t1v = 0.0f;
+    if constexpr (W == kHalf && last) {
+      a_tv = *park(1);
+      a_t1v = *park(2);
+    }
+    if (CSA && first) mx = fmaxf(mx, a0v);
+    if (W == kHalf && last && qrow() != Tn - 1) mx = fmaxf(mx, a_t1v);  // position t + 1 takes a weight
     // the shift moves only if some lane's own maximum passes m_run + 8 (the same test as on
     // the query-wide maximum, which is the largest of its lanes'); only then the maximum over
     // the query's four lanes, and every query of the wave takes its new shift (unchanged
@@ -534,10 +603,10 @@ __global__ void __launch_bounds__(512, 4) attn16_kernel(FwdParams p) {
       float left = from_lane(lane_up(), lsend);
       float right = from_lane(lane_dn(), s[0]);
       carry_s = s[15];
-      if (first && g == 0) left = a0;
+      if (first && g == 0) left = a0v;
       if (!last && g == 3) right = halo;
-      if (first)  // position 0 has only its right neighbour, the first key (lanes g = 0)
-        w0 = exp2_fast(__builtin_fmaf(4.0f, beta(a0), __builtin_fmaf(2.0f, beta(s[0]), -1.0f)));
+      if (first && g == 0)  // position 0 has only its right neighbour, the first key
+        *park(4) = exp2_fast(__builtin_fmaf(4.0f, beta(a0v), __builtin_fmaf(2.0f, beta(s[0]), -1.0f)));
       float bl = beta(left);
       float bc = beta(s[0]);
 #pragma unroll
@@ -579,26 +648,28 @@ __global__ void __launch_bounds__(512, 4) attn16_kernel(FwdParams p) {
       float Lprev = from_lane(lane_up(), Lsend);
       carry = Lnext;  // lanes g = 3: left term of key 64(j+1)
       if (first) {    // position 0: only its right neighbour (eq. (10), i = 0)
-        const float a0l = __builtin_fmaf(a0, kLog2e, -mr);
+        const float a0l = __builtin_fmaf(a0v, kLog2e, -mr);
         float R0, L1;
         if constexpr (W == kHalf) half::upper_half(a0l, exp2_fast(a0l), al0, pv0, R0, L1);
         else edge_terms<false>(a0l, exp2_fast(a0l), al0, pv0, R0, L1);
-        w0 = R0;
-        if (g == 0) Lprev = L1;
+        if (g == 0) {
+          *park(4) = R0;
+          Lprev = L1;
+        }
       }
       // interval variant, diagonal tile: the lower half of segment (t, t+1) -- HR to the
       // query's own key (column lim), HL to the next (column lim + 1, or the next tile's
       // first key when lim = 15 in lane group 3: added in the epilogue)
       float hR = 0.0f, hL = 0.0f;
       if constexpr (W == kHalf && last) {
-        const float alt = __builtin_fmaf(a_t, kLog2e, -mr);
+        const float alt = __builtin_fmaf(a_tv, kLog2e, -mr);
         const float ptv = exp2_fast(alt);
-        half::lower_half(alt, ptv, __builtin_fmaf(a_t1, kLog2e, -mr), hR, hL);
-        if (lastq) {  // position T+1 repeats T: the whole half segment goes to T
+        half::lower_half(alt, ptv, __builtin_fmaf(a_t1v, kLog2e, -mr), hR, hL);
+        if (qrow() == Tn - 1) {  // position T+1 repeats T: the whole half segment goes to T
           hR = 0.5f * half::kC2 * ptv;
           hL = 0.0f;
         }
-        if (g == 3 && lim == 15) hl_next = hL;
+        if (g == 3) *park(3) = lim == 15 ? hL : 0.0f;  // HL of the next tile's first key
       }
       // edge (t, t+1) needs p_t, p_{t+1}, y_t = alpha_{t+1} - alpha_t and 1/y_t; the
       // values of key t+2 are formed one step ahead
@@ -651,10 +722,7 @@ __global__ void __launch_bounds__(512, 4) attn16_kernel(FwdParams p) {
     for (int u = 0; u < NP; ++u) pv_unit(1, u, P1);
   };
 
-  // ---- prologue: K_0, V_0, K_1 into LDS; S^T of tile 0
-  stage(0, Kg, 0, false);
-  stage(2, Vg, 0, true);
-  if (jmax >= 1) stage(1, Kg, 1, false);
+  // ---- prologue: S^T of tile 0 (its copies were issued first)
   wait_vmem();
   __syncthreads();
   f32x4 SA[4], SB[4];
@@ -714,26 +782,28 @@ __global__ void __launch_bounds__(512, 4) attn16_kernel(FwdParams p) {
   float l = qsum(lsum);
   float w0q = 0.0f;
   if (CSA) {
-    w0q = from_lane(n, w0);
+    w0q = *park(4);
     l += w0q;
   }
   if constexpr (W == kHalf) {
-    if (((qw + 15) & 63) == 63) {  // wave-uniform: its last query's t + 1 opens the next tile
-      const float wn = from_lane(48 + n, hl_next);
+    if (vrow_wave) {  // its last query's t + 1 opens the next tile
+      const float wn = *park(3);
       l += wn;
-      const bf16* Vn = (const bf16*)p.v + head + (size_t)min(qr + 1, Tn - 1) * D;
+      // the row of the wave's query 15, the only one whose wn is not zero
+      CSA_LDS const bf16* Vn = (CSA_LDS const bf16*)vnext + D * wave;
 #pragma unroll
       for (int mb = 0; mb < NMB; ++mb) {
-        const bf16x4 vn = *(const bf16x4*)(Vn + 16 * mb + 4 * g);
+        const bf16x4 vn = *(CSA_LDS const bf16x4*)(Vn + 16 * mb + 4 * g);
 #pragma unroll
         for (int r = 0; r < 4; ++r) O[mb][r] = __builtin_fmaf(wn, (float)vn[r], O[mb][r]);
       }
     }
   }
   const float inv = 1.0f / l;
-  if (qr < Tn) {
+  const int qe = qrow();
+  if (qe < Tn) {
     const bf16* V0 = (CSA && p.v0 != nullptr) ? (const bf16*)p.v0 + (size_t)bh * D : nullptr;
-    bf16* Og = (bf16*)p.out + head + (size_t)qr * D;
+    bf16* Og = (bf16*)p.out + head + (size_t)qe * D;
 #pragma unroll
     for (int mb = 0; mb < NMB; ++mb) {
       const int d0 = 16 * mb + 4 * g;
@@ -748,7 +818,7 @@ __global__ void __launch_bounds__(512, 4) attn16_kernel(FwdParams p) {
     }
     if (p.lse != nullptr && g == 0) {
       const float corr = (W == kExact || W == kHalf) ? 0.7330258411633287f : 0.0f;  // -2 ln(ln 2)
-      p.lse[(size_t)bh * Tn + qr] = (m_run + __builtin_amdgcn_logf(l)) * kLn2 + corr;
+      p.lse[(size_t)bh * Tn + qe] = (m_run + __builtin_amdgcn_logf(l)) * kLn2 + corr;
     }
   }
 }

@@ -349,17 +349,19 @@ __global__ void __launch_bounds__(512, 4) attn16_kernel(FwdParams p) {
   // this lane's query row, formed from the lane index where used (not kept across the loop)
   auto qrow = [&]() { return qw + (lane_here() & 15); };
 
-  // interval variant: key rows qr (position t) and qr + 1 (position t + 1), whose logits
-  // the lower half of segment (t, t+1) on the diagonal tile needs; loaded before the k0 row
-  // so that all of the prologue's loads are in flight at once
-  bf16x8 kt[W == kHalf ? NSTEP : 1], kn[W == kHalf ? NSTEP : 1];
-  // and, when the wave's last query's position t + 1 opens the next tile (wave-uniform), the
-  // value row of that position, one 4-byte piece per lane, for `vnext`
-  const bool vrow_wave = W == kHalf && ((qw + 15) & 63) == 63;
-  unsigned vpiece = 0;
-  if (vrow_wave && lane_here() < D / 2)
-    vpiece = *(const unsigned*)((const bf16*)p.v + head + (size_t)min(qw + 16, Tn - 1) * D +
-                                2 * lane_here());
+  // ---- the prologue's own loads, all issued before any of them is waited for: the key of
+  // position 0 and, for the interval variant, the key rows qr (position t) and qr + 1
+  // (position t + 1), whose logits the lower half of segment (t, t+1) on the diagonal tile
+  // needs, and -- when the wave's last query's position t + 1 opens the next tile (wave-
+  // uniform) -- the value row of that position, one 4-byte piece per lane, for `vnext`
+  const bool have_k0 = CSA && p.k0 != nullptr;
+  // without k0 any readable row serves (the product is discarded): the loads stay unconditional
+  const bf16* K0 = have_k0 ? (const bf16*)p.k0 + (size_t)bh * D : (const bf16*)p.q + head;
+  bf16x8 kc[NSTEP], kt[W == kHalf ? NSTEP : 1], kn[W == kHalf ? NSTEP : 1];
+#pragma unroll
+  for (int s = 0; s < NSTEP; ++s) {
+    if (CSA && 4 * s + g < CH) kc[s] = *(const bf16x8*)(K0 + (4 * s + g) * 8);
+  }
   if constexpr (W == kHalf) {
     const bf16* Kh = (const bf16*)p.k + head;
     const int rt = min(qr, Tn - 1), rn = min(qr + 1, Tn - 1);
@@ -371,21 +373,24 @@ __global__ void __launch_bounds__(512, 4) attn16_kernel(FwdParams p) {
       }
     }
   }
+  const bool vrow_wave = W == kHalf && ((qw + 15) & 63) == 63;
+  unsigned vpiece = 0;
+  if (vrow_wave && lane_here() < D / 2)
+    vpiece = *(const unsigned*)((const bf16*)p.v + head + (size_t)min(qw + 16, Tn - 1) * D +
+                                2 * lane_here());
 
   // ---- logit of position 0: a0 = q . k0 (zero when k0 is null)
   float a0 = 0.0f;
-  if (CSA && p.k0 != nullptr) {
-    const bf16* K0 = (const bf16*)p.k0 + (size_t)bh * D;
+  if constexpr (CSA) {
     float part = 0.0f;
 #pragma unroll
     for (int s = 0; s < NSTEP; ++s) {
       if (4 * s + g < CH) {
-        const bf16x8 kc = *(const bf16x8*)(K0 + (4 * s + g) * 8);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) part = __builtin_fmaf((float)qreg[s][e], (float)kc[e], part);
+        for (int e = 0; e < 8; ++e) part = __builtin_fmaf((float)qreg[s][e], (float)kc[s][e], part);
       }
     }
-    a0 = qsum(part);
+    a0 = have_k0 ? qsum(part) : 0.0f;
   }
   if (CSA) *park(0) = a0;
   float a_t = 0.0f, a_t1 = 0.0f;
@@ -616,9 +621,9 @@ __global__ void __launch_bounds__(512, 4) attn16_kernel(FwdParams p) {
         if constexpr (!last) {
           wv = exp2_fast(__builtin_fmaf(4.0f, bc, bl + bn));
         } else {  // diagonal tile: column t takes the end rule, columns > t get 0
-          const float wi = exp2_fast(__builtin_fmaf(4.0f, bc, bl + bn));
-          const float we = exp2_fast(__builtin_fmaf(4.0f, bc, __builtin_fmaf(2.0f, bl, -1.0f)));
-          wv = t < lim ? wi : (t == lim ? we : 0.0f);
+          const float x = t < lim ? bl + bn : __builtin_fmaf(2.0f, bl, -1.0f);
+          const float we = exp2_fast(__builtin_fmaf(4.0f, bc, x));
+          wv = t <= lim ? we : 0.0f;
         }
         w[t] = wv;
         bl = bc;

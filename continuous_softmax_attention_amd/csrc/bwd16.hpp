@@ -854,6 +854,11 @@ __global__ void __launch_bounds__(512, 4) bwd_dkdv_kernel(BwdParams p) {
     const int rowc = min(qr, Tn - 1);
     float s[16], dp[16];
     f32x4 Hs, Hd;
+    // The logits products run at the lowest wave priority and the rest of the block at the
+    // next one, so that a SIMD issues its other waves' gradient (VALU) work ahead of a wave's
+    // logits (A/B on lm: about 1% faster than equal priorities; prioritising the products
+    // instead was 1% slower).
+    __builtin_amdgcn_s_setprio(0);
     {
       bf16x8 qreg[NSTEP];
 #pragma unroll
@@ -867,6 +872,7 @@ __global__ void __launch_bounds__(512, 4) bwd_dkdv_kernel(BwdParams p) {
       for (int st = 0; st < NSTEP; ++st) dreg[st] = *(const bf16x8*)(Og + (rowc * ROWB + (4 * st + g) * 16));
       logits_tile<D>(lds + OFF_V, lds + OFF_VH, kbase, hoff, dreg, dp, Hd);
     }
+    __builtin_amdgcn_s_setprio(1);
     const float mu = (ws.mu + (size_t)bh * Tn)[rowc];
     const float delta = (ws.delta + (size_t)bh * Tn)[rowc];
     float sl, sr, dl, dr;

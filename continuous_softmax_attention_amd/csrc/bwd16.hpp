@@ -25,10 +25,10 @@
 // c_e = p_i (c^2/6 + c^3 y/12 + c^4 y^2/40).
 //
 // Kernels (one launch each, in this order on the caller's stream):
-//   bwd_pre   D_t = dO_t . o_t and mu_t into the workspace; zero rows standing in for a
-//             null k_0 / v_0.
 //   bwd_transpose  Q^T and dO^T ([B*H][D][T rounded up to 128], zeros past T) into the
-//             workspace: the A operands of bwd_dkdv's dK / dV products.
+//             workspace: the A operands of bwd_dkdv's dK / dV products; its dO work-groups
+//             also write D_t = dO_t . o_t and mu_t, and work-group 0 the zero rows standing in
+//             for a null k_0 / v_0.
 //   bwd_dq    one work-group per 128 query rows (the forward's decomposition: 8 waves x
 //             16 queries, 64-key tiles double-buffered in LDS).  Per tile S^T = K Q^T and
 //             dP^T = V dO^T on MFMAs, plus one 16-row "halo" block whose rows 0 and 1 are
@@ -414,32 +414,6 @@ __device__ __forceinline__ void stage_tile(CSA_LDS char* dst, const char* src, i
 
 // ---------------------------------------------------------------- kernels
 template <int D>
-__global__ void __launch_bounds__(256) bwd_pre_kernel(BwdParams p) {
-  constexpr int CH = D / 8;
-  constexpr int RPW = 64 / CH;  // rows per wave
-  const int BH = p.B * p.H, T = p.T;
-  const BwdWs w = bwd_ws(p.ws, BH, T, D);
-  if (blockIdx.x == 0 && threadIdx.x < kBwdZeroBytes / 4) ((float*)p.ws)[threadIdx.x] = 0.0f;
-  const int lane = threadIdx.x & 63;
-  const int64_t nrows = (int64_t)BH * T;
-  const int64_t row = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * RPW + lane / CH;
-  const int c = lane % CH;
-  float acc = 0.0f;
-  if (row < nrows) {
-    const bf16x8 a = *(const bf16x8*)((const bf16*)p.dout + row * D + c * 8);
-    const bf16x8 b = *(const bf16x8*)((const bf16*)p.o + row * D + c * 8);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) acc = __builtin_fmaf((float)a[e], (float)b[e], acc);
-  }
-#pragma unroll
-  for (int m = 1; m < CH; m <<= 1) acc += __shfl_xor(acc, m);
-  if (row < nrows && c == 0) {
-    w.delta[row] = acc;
-    w.mu[row] = __builtin_fmaf(p.lse[row], kLog2e, kMuShift);
-  }
-}
-
-template <int D>
 __global__ void __launch_bounds__(512, 2) bwd_dq_kernel(BwdParams p) {
   using WT = WaveTile<D>;
   constexpr int CH = WT::CH, ROWB = WT::ROWB, NSTEP = WT::NSTEP, NMB = WT::NMB;
@@ -739,6 +713,7 @@ __global__ void __launch_bounds__(256) bwd_transpose_kernel(BwdParams p) {
   const int which = blockIdx.x & 1, tile = (blockIdx.x >> 1) % ntile, bh = (blockIdx.x >> 1) / ntile;
   const BwdWs ws = bwd_ws(p.ws, BH, Tn, D);
   const bf16* src = (const bf16*)(which ? p.dout : p.q) + (size_t)bh * Tn * D;
+  if (blockIdx.x == 0 && threadIdx.x < kBwdZeroBytes / 4) ((float*)p.ws)[threadIdx.x] = 0.0f;
   for (int i = threadIdx.x; i < 64 * D / 8; i += 256) {
     const int r = i / (D / 8), c = i % (D / 8), t = tile * 64 + r;
     uint4 v = {0u, 0u, 0u, 0u};
@@ -748,6 +723,22 @@ __global__ void __launch_bounds__(256) bwd_transpose_kernel(BwdParams p) {
     w[1] = v.y;
     w[2] = v.z;
     w[3] = v.w;
+    if (which) {  // the dO work-groups also form D_t = dO_t . o_t and mu_t of their rows
+      float acc = 0.0f;
+      if (t < Tn) {
+        const bf16x8 a = __builtin_bit_cast(bf16x8, v);
+        const bf16x8 b = *(const bf16x8*)((const bf16*)p.o + (size_t)bh * Tn * D + (size_t)t * D + 8 * c);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc = __builtin_fmaf((float)a[e], (float)b[e], acc);
+      }
+#pragma unroll
+      for (int m = 1; m < D / 8; m <<= 1) acc += __shfl_xor(acc, m);  // the D/8 lanes of row r
+      if (t < Tn && c == 0) {
+        const size_t row = (size_t)bh * Tn + t;
+        ws.delta[row] = acc;
+        ws.mu[row] = __builtin_fmaf(p.lse[row], kLog2e, kMuShift);
+      }
+    }
   }
   __syncthreads();
   bf16* dst = (which ? ws.dot : ws.qt) + (size_t)bh * D * Tp + tile * 64;
@@ -955,12 +946,9 @@ template <int D>
 inline hipError_t launch_backward(const BwdParams& prm_in, hipStream_t stream) {
   BwdParams prm = prm_in;
   const int BH = prm.B * prm.H;
-  const int64_t rows = (int64_t)BH * prm.T;
-  const int rpb = 4 * (64 / (D / 8));  // rows per pre block
   const int group = prm.nh;
   prm.h0 = 0;
   prm.nh = BH;
-  hipLaunchKernelGGL((bwd_pre_kernel<D>), dim3((unsigned)((rows + rpb - 1) / rpb)), dim3(256), 0, stream, prm);
   hipLaunchKernelGGL((bwd_transpose_kernel<D>), dim3((unsigned)(BH * (bwd_tp(prm.T) / 64) * 2)), dim3(256), 0, stream,
                      prm);
   const int nqb = (prm.T + kBlockRows - 1) / kBlockRows;

@@ -4,7 +4,7 @@
 // no bf16 rounding of P or dS.  These shapes are small (the float32 workloads are at most
 // 4 heads of 1024 rows), so the kernels are written for clarity and exactness first:
 //
-//   bwdv_pre   D_t = dO_t . o_t and mu_t = log2(c^2 Z_t) from the forward's lse (as bwd_pre).
+//   bwdv_pre   D_t = dO_t . o_t and mu_t = log2(c^2 Z_t) from the forward's lse (as bwd_transpose does for bf16).
 //   bwdv_dq    one wave per query t: the positions 0..t in chunks of 62, lane j holding
 //              position base - 1 + j (neighbours in lanes j -+ 1); its logit a_{t,i} and
 //              dO_t . v_i by dot products, P and dS from the edge terms; dq_t = sum_i dS_{t,i} k_i

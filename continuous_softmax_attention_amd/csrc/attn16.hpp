@@ -106,6 +106,34 @@ __device__ __forceinline__ void edge_yu(float pl, float pr, float y, float u, fl
   L_right = small ? lt : lr;
 }
 
+// The same edge for the off-diagonal tiles, with the series formed only when some lane of the
+// wave has |y| < kY0Ballot (a wave-uniform branch on the compare's lane mask).  Between
+// kY0Ballot and Taylor<false>::Y0 the closed form is kept: its cancellation turns the two exp2
+// roundings (up to 1 ulp each) into a relative error of about 1e-6 / y^2 on R and L, at most
+// 3.3e-3 at |y| = 0.02 in a float32 emulation, which is under the bf16 rounding (up to 2^-8
+// relative) that every weight takes before the P V product.  Such small neighbour differences
+// are rare at the logit scales of attention, so most waves skip the series on most keys.
+constexpr float kY0Ballot = 0.02f;
+__device__ __forceinline__ void edge_yu_ballot(float pl, float pr, float y, float u, float Lprev,
+                                               float& w_left, float& L_right) {
+  const float du = (pr - pl) * u;
+  w_left = __builtin_fmaf(__builtin_fmaf(-kLn2, pl, du), u, Lprev);
+  L_right = __builtin_fmaf(kLn2, pr, -du) * u;
+  const bool small = __builtin_fabsf(y) < kY0Ballot;
+  if (__builtin_amdgcn_ballot_w64(small) != 0) {
+    // opaque copies keep the series inside the branch (otherwise it is hoisted above it and
+    // the branch becomes two selects on every key)
+    float ys = y, pls = pl, prs = pr;
+    asm volatile("" : "+v"(ys), "+v"(pls), "+v"(prs));
+    float gp, gm;
+    Taylor<false>::eval(ys, gp, gm);
+    const float wt = __builtin_fmaf(pls, gp, Lprev);
+    const float lt = prs * gm;
+    w_left = small ? wt : w_left;
+    L_right = small ? lt : L_right;
+  }
+}
+
 // Work-group i -> (head bh, rank of its block among the head's nblk blocks, 0 = the most work).
 // Work-groups go to the 8 XCDs round robin (i -> XCD i mod 8), each XCD with its own 4 MB L2.
 // With B*H a multiple of 8 * G, XCD x takes its heads x, x+8, x+16, ... G at a time, each group's
@@ -697,7 +725,7 @@ __global__ void __launch_bounds__(512, 4) attn16_kernel(FwdParams p) {
             un = __builtin_amdgcn_rcpf(yn);
           }
           if constexpr (!last) {
-            edge_yu(pc, pn, yc, uc, Lprev, w[t], Lprev);
+            edge_yu_ballot(pc, pn, yc, uc, Lprev, w[t], Lprev);
           } else {  // diagonal tile: column t keeps only its left term, columns > t get 0
             float R, L;
             edge_yu(pc, pn, yc, uc, 0.0f, R, L);

@@ -61,6 +61,31 @@ def _random_case(B, H, T, d, dtype, seed, q_mult=1.0, sink=True):
     return cast(q), cast(k), cast(v), cast(k0), cast(v0)
 
 
+@pytest.mark.parametrize("rule", ["exact", "half_interval"])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("q_mult", [0.01, 0.02, 0.04])
+def test_small_neighbour_differences_bf16(q_mult, d, rule):
+    # logit std ~ q_mult: most neighbour differences y (base-2 units) fall below 0.1, where the
+    # edge terms' closed form cancels; the bf16 kernels take the series below |y| < 0.02 on the
+    # off-diagonal tiles (below 0.07 on the diagonal one) and the closed form above
+    from oracle import csa_half_reference
+    fn, ref = {"exact": (csa.csa_forward, csa_reference),
+               "half_interval": (csa.csa_forward_half_interval, csa_half_reference)}[rule]
+    q, k, v, k0, v0 = _random_case(1, 3, 333, d, torch.bfloat16, seed=int(5000 * q_mult) + d, q_mult=q_mult)
+    a = torch.einsum("bhtd,bhsd->bhts", q.double(), k.double())
+    y = (a[..., 1:] - a[..., :-1]).abs() / math.log(2.0)
+    causal = torch.ones(333, 332, dtype=torch.bool).tril()
+    band = float(((y >= 0.02) & (y < 0.07))[..., causal].double().mean())
+    assert band > 0.25  # the case exercises the band between the two thresholds
+    o, lse = fn(*_gpu(q, k, v, k0, v0))
+    torch.cuda.synchronize()
+    o, lse = o.float().cpu().double().numpy(), lse.cpu().double().numpy()
+    o_ref, l_ref = ref(q, k, v, k0, v0)
+    eo, el = _errs(o, lse, o_ref, l_ref)
+    _report(f"small differences x{q_mult} d{d} {rule} (band fraction {band:.2f})", eo, el)
+    assert eo <= TOL[torch.bfloat16] and el <= TOL[torch.bfloat16]
+
+
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16], ids=["f32", "bf16"])
 @pytest.mark.parametrize("d", [16, 64, 128])
 @pytest.mark.parametrize("T", [1, 2, 3, 31, 32, 33, 63, 64, 65, 127, 128, 129, 200, 257])

@@ -121,14 +121,14 @@ __device__ __forceinline__ void edge_yu_ballot(float pl, float pr, float y, floa
   L_right = __builtin_fmaf(kLn2, pr, -du) * u;
   const bool small = __builtin_fabsf(y) < kY0Ballot;
   if (__builtin_amdgcn_ballot_w64(small) != 0) {
-    // opaque copies keep the series inside the branch (otherwise it is hoisted above it and
-    // the branch becomes two selects on every key)
-    float ys = y, pls = pl, prs = pr;
-    asm volatile("" : "+v"(ys), "+v"(pls), "+v"(prs));
+    // an opaque copy of y keeps the series inside the branch (otherwise it is hoisted above
+    // it and the branch becomes two selects on every key)
+    float ys = y;
+    asm volatile("" : "+v"(ys));
     float gp, gm;
     Taylor<false>::eval(ys, gp, gm);
-    const float wt = __builtin_fmaf(pls, gp, Lprev);
-    const float lt = prs * gm;
+    const float wt = __builtin_fmaf(pl, gp, Lprev);
+    const float lt = pr * gm;
     w_left = small ? wt : w_left;
     L_right = small ? lt : L_right;
   }
@@ -674,7 +674,12 @@ __global__ void __launch_bounds__(512, 4) attn16_kernel(FwdParams p) {
         }
       }
       float R15, Lnext;
-      edge_terms<false>(al15, pv15, ar, pr, R15, Lnext);
+      if constexpr (last) {
+        edge_terms<false>(al15, pv15, ar, pr, R15, Lnext);
+      } else {
+        const float y15 = ar - al15;
+        edge_yu_ballot(pv15, pr, y15, __builtin_amdgcn_rcpf(y15), 0.0f, R15, Lnext);
+      }
       // left term of key 0: from the previous group, or (g = 0) carried from the
       // previous tile's group 3, or (first tile) from the edge with position 0
       const float Lsend = g == 3 ? carry : Lnext;

@@ -239,23 +239,25 @@ __device__ __forceinline__ void edge_grad(float al, float pl, float ar, float pr
 }
 
 // P and dS of one lane's 16 consecutive keys base+t of its query, rounded to bf16 (to nearest
-// even) as they are formed: P8[h][e], dS8[h][e] for key base + 8h + e.  s/dp: logits and dO.v
-// of those keys; sl, dpl and sr, dpr: the same for keys base-1 and base+16.  Key base+t is
+// even) as they are formed: P8[h][e], dS8[h][e] for key base + 8h + e.  s/dp: logits and
+// dO.v - D_t of those keys (the dP products start from -D_t: the softmax term of dS is then
+// P dp, and the differences of dp in the edge terms do not change); sl, dpl and sr, dpr: the
+// same for keys base-1 and base+16.  Key base+t is
 // visible iff t <= lim.  Also returns P and dS of key base-1 (float) as they follow from its
 // right edge alone: exact when key base-1 is position 0 (which has no left edge).
 // MASKED = false when every key of the tile and its right neighbour are visible (lim >= 16 in
 // every lane).
 template <bool MASKED, typename Emit>
 __device__ __forceinline__ void tile_grad(const float (&s)[16], const float (&dp)[16], float sl, float dpl,
-                                          float sr, float dpr, float mu, float delta, int lim, Emit&& emit,
+                                          float sr, float dpr, float mu, int lim, Emit&& emit,
                                           float& p_left, float& ds_left) {
 #pragma clang fp contract(off)
   bf16x8 P8, dS8;
   // Opaque copies of the inputs: callers inline the masked and the unmasked form behind one
   // branch, and without them the compiler computed everything the two forms share (every
   // exponential and difference of the tile) above the branch, all live at once (spills).
-  float mu_o = mu, delta_o = delta, dpl_o = dpl, dpr_o = dpr;
-  asm volatile("" : "+v"(mu_o), "+v"(delta_o), "+v"(dpl_o), "+v"(dpr_o));
+  float mu_o = mu, dpl_o = dpl, dpr_o = dpr;
+  asm volatile("" : "+v"(mu_o), "+v"(dpl_o), "+v"(dpr_o));
   float dpo[16];
 #pragma unroll
   for (int t = 0; t < 16; ++t) {
@@ -269,7 +271,7 @@ __device__ __forceinline__ void tile_grad(const float (&s)[16], const float (&dp
   edge_grad<MASKED>(aC, pC, aN, pN, 0 <= lim, 0.0f, W, L, C);
   float G = C * (dC - dN);
   p_left = W;
-  ds_left = __builtin_fmaf(W, dC - delta_o, -G);
+  ds_left = __builtin_fmaf(W, dC, -G);
   float Lprev = L, Gprev = G;
   aC = aN;
   pC = pN;
@@ -287,7 +289,7 @@ __device__ __forceinline__ void tile_grad(const float (&s)[16], const float (&dp
     edge_grad<MASKED>(aC, pC, aN, pN, t + 1 <= lim, Lprev, W, L, C);
     G = C * (dC - dN);
     P8[t & 7] = (bf16)W;
-    dS8[t & 7] = (bf16)__builtin_fmaf(W, dC - delta_o, Gprev - G);
+    dS8[t & 7] = (bf16)__builtin_fmaf(W, dC, Gprev - G);
     if ((t & 7) == 7) emit(t >> 3, P8, dS8);  // keys 8h .. 8h + 7 done
     if ((t & 3) == 3) __builtin_amdgcn_sched_barrier(0);  // bounds how far work is hoisted (registers)
     Lprev = L;
@@ -333,18 +335,20 @@ __device__ __forceinline__ void tr_vbase(int n, int g, int (&vb)[2]) {
 // (rows 0, 1 = keys J-1, J+64) -> lanes g = 0 get them in elements 0 and 1.
 template <int D>
 __device__ __forceinline__ void logits_tile(CSA_LDS const char* tile, CSA_LDS const char* halo, int kbase,
-                                            int hoff, const bf16x8 (&b)[D / 32], float (&s)[16], f32x4& H) {
+                                            int hoff, const bf16x8 (&b)[D / 32], float c0, float (&s)[16],
+                                            f32x4& H) {
   constexpr int NSTEP = D / 32;
+  const f32x4 init = {c0, c0, c0, c0};  // every accumulator element belongs to the lane's query
   f32x4 S[4];
 #pragma unroll
   for (int blk = 0; blk < 4; ++blk) {
-    S[blk] = f32x4{};
+    S[blk] = init;
 #pragma unroll
     for (int st = 0; st < NSTEP; ++st)
       S[blk] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(row_read(tile, kbase, st, blk), b[st], S[blk], 0, 0, 0);
     __builtin_amdgcn_sched_barrier(0);  // one block's operands in flight at a time (register pressure)
   }
-  H = f32x4{};
+  H = init;
 #pragma unroll
   for (int st = 0; st < NSTEP; ++st) {
     const bf16x8 a = *(CSA_LDS const bf16x8*)(halo + hoff + st * 64);
@@ -503,8 +507,8 @@ __global__ void __launch_bounds__(512, 2) bwd_dq_kernel(BwdParams p) {
       CSA_LDS const char* b = lds + (j & 1) * BUF;
       float s[16], dp[16];
       f32x4 Hs, Hd;
-      logits_tile<D>(b, b + 3 * TILE, kbase, hoff, qreg, s, Hs);
-      logits_tile<D>(b + 2 * TILE, b + 3 * TILE + HALO, kbase, hoff, dreg, dp, Hd);
+      logits_tile<D>(b, b + 3 * TILE, kbase, hoff, qreg, 0.0f, s, Hs);
+      logits_tile<D>(b + 2 * TILE, b + 3 * TILE + HALO, kbase, hoff, dreg, -delta, dp, Hd);
       float sl, sr, dl, dr;
       neighbours(s, Hs, n, g, sl, sr);
       neighbours(dp, Hd, n, g, dl, dr);
@@ -514,8 +518,8 @@ __global__ void __launch_bounds__(512, 2) bwd_dq_kernel(BwdParams p) {
       auto keep = [&](int h, const bf16x8&, const bf16x8& ds) { dS8[h] = ds; };
       // every edge of the tile exists for every query of the wave (rows past T only feed
       // their own, unstored, dq rows)
-      if ((j + 1) * kTile <= qw) tile_grad<false>(s, dp, sl, dl, sr, dr, mu, delta, lim, keep, pl, dsl);
-      else tile_grad<true>(s, dp, sl, dl, sr, dr, mu, delta, lim, keep, pl, dsl);
+      if ((j + 1) * kTile <= qw) tile_grad<false>(s, dp, sl, dl, sr, dr, mu, lim, keep, pl, dsl);
+      else tile_grad<true>(s, dp, sl, dl, sr, dr, mu, lim, keep, pl, dsl);
       if (j == 0) {
         p0 = pl;
         ds0 = dsl;
@@ -854,18 +858,18 @@ __global__ void __launch_bounds__(512, 4) bwd_dkdv_kernel(BwdParams p) {
       bf16x8 qreg[NSTEP];
 #pragma unroll
       for (int st = 0; st < NSTEP; ++st) qreg[st] = *(const bf16x8*)(Qg + (rowc * ROWB + (4 * st + g) * 16));
-      logits_tile<D>(lds, lds + OFF_KH, kbase, hoff, qreg, s, Hs);
+      logits_tile<D>(lds, lds + OFF_KH, kbase, hoff, qreg, 0.0f, s, Hs);
     }
     __builtin_amdgcn_sched_barrier(0);
     {
       bf16x8 dreg[NSTEP];
 #pragma unroll
       for (int st = 0; st < NSTEP; ++st) dreg[st] = *(const bf16x8*)(Og + (rowc * ROWB + (4 * st + g) * 16));
-      logits_tile<D>(lds + OFF_V, lds + OFF_VH, kbase, hoff, dreg, dp, Hd);
+      const float delta = (ws.delta + (size_t)bh * Tn)[rowc];
+      logits_tile<D>(lds + OFF_V, lds + OFF_VH, kbase, hoff, dreg, -delta, dp, Hd);
     }
     __builtin_amdgcn_s_setprio(1);
     const float mu = (ws.mu + (size_t)bh * Tn)[rowc];
-    const float delta = (ws.delta + (size_t)bh * Tn)[rowc];
     float sl, sr, dl, dr;
     neighbours(s, Hs, n, g, sl, sr);
     neighbours(dp, Hd, n, g, dl, dr);
@@ -884,8 +888,8 @@ __global__ void __launch_bounds__(512, 4) bwd_dkdv_kernel(BwdParams p) {
     // every edge exists for every query of the wave, and no row of the wave lies past T
     // (those rows must contribute zeros to dK and dV)
     const int qw = Q0 + 16 * wave;
-    if (qw >= J + kTile && qw + 15 < Tn) tile_grad<false>(s, dp, sl, dl, sr, dr, mu, delta, lim, emit, pl, dsl);
-    else tile_grad<true>(s, dp, sl, dl, sr, dr, mu, delta, lim, emit, pl, dsl);
+    if (qw >= J + kTile && qw + 15 < Tn) tile_grad<false>(s, dp, sl, dl, sr, dr, mu, lim, emit, pl, dsl);
+    else tile_grad<true>(s, dp, sl, dl, sr, dr, mu, lim, emit, pl, dsl);
     if constexpr (WRITE_DS) {
       if (J == 0 && g == 0 && qr < Tn) {
         (ws.p0 + (size_t)bh * Tn)[qr] = pl;

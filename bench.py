@@ -66,9 +66,9 @@ def _cpu_task(args):
     return int(np.sum(rows + 1))
 
 
-# Worker processes of the CPU leg: the GPU machine gives one GPU a share of 16 host cores, whatever
-# os.sched_getaffinity shows there (the whole host's cores may be listed), so the pool takes at
-# most 16; the host's own count is reported beside it.
+# Worker processes of the CPU leg: one GPU's share of the host is 16 cores, whatever
+# os.sched_getaffinity shows (it may list every core of the host), so the pool takes at most 16;
+# the affinity mask's own count is reported beside it.
 CPU_WORKERS_MAX = 16
 
 
@@ -112,7 +112,7 @@ def cpu_baseline(w, q, k, v, k0, v0, heads=64, rows_per_head=320, seed=123):
         "sample": (f"{len(tasks)} of {nheads} heads x {rows_per_head} seeded query rows "
                    f"({len(tasks) * rows_per_head} of {total_rows} rows), float64 eq. (8), "
                    f"{workers} worker processes (of {host_cores} cores in the affinity mask; "
-                   f"one GPU's share of the box is {CPU_WORKERS_MAX}), {dt:.1f} s wall"),
+                   f"one GPU's share of the host is {CPU_WORKERS_MAX}), {dt:.1f} s wall"),
         "sample_s": round(dt, 2),
         # the whole workload at the sampled rate (row cost grows with t + 1, counted in the FLOP)
         "extrapolated_full_s": round(float(w.flop) / rate, 1),

@@ -854,22 +854,22 @@ __global__ void __launch_bounds__(512, 4) bwd_dkdv_kernel(BwdParams p) {
     // logits (A/B on lm: about 1% faster than equal priorities; prioritising the products
     // instead was 1% slower).
     __builtin_amdgcn_s_setprio(0);
+    bf16x8 dreg[NSTEP];
+    float delta, mu;
     {
       bf16x8 qreg[NSTEP];
 #pragma unroll
       for (int st = 0; st < NSTEP; ++st) qreg[st] = *(const bf16x8*)(Qg + (rowc * ROWB + (4 * st + g) * 16));
+      // the dO rows are issued with the Q rows, so that their latency passes under the S product
+#pragma unroll
+      for (int st = 0; st < NSTEP; ++st) dreg[st] = *(const bf16x8*)(Og + (rowc * ROWB + (4 * st + g) * 16));
+      delta = (ws.delta + (size_t)bh * Tn)[rowc];
+      mu = (ws.mu + (size_t)bh * Tn)[rowc];
       logits_tile<D>(lds, lds + OFF_KH, kbase, hoff, qreg, 0.0f, s, Hs);
     }
     __builtin_amdgcn_sched_barrier(0);
-    {
-      bf16x8 dreg[NSTEP];
-#pragma unroll
-      for (int st = 0; st < NSTEP; ++st) dreg[st] = *(const bf16x8*)(Og + (rowc * ROWB + (4 * st + g) * 16));
-      const float delta = (ws.delta + (size_t)bh * Tn)[rowc];
-      logits_tile<D>(lds + OFF_V, lds + OFF_VH, kbase, hoff, dreg, -delta, dp, Hd);
-    }
+    logits_tile<D>(lds + OFF_V, lds + OFF_VH, kbase, hoff, dreg, -delta, dp, Hd);
     __builtin_amdgcn_s_setprio(1);
-    const float mu = (ws.mu + (size_t)bh * Tn)[rowc];
     float sl, sr, dl, dr;
     neighbours(s, Hs, n, g, sl, sr);
     neighbours(dp, Hd, n, g, dl, dr);

@@ -842,6 +842,12 @@ __global__ void __launch_bounds__(512, 4) attn16_kernel(FwdParams p) {
   if (qe < Tn) {
     const bf16* V0 = (CSA && p.v0 != nullptr) ? (const bf16*)p.v0 + (size_t)bh * D : nullptr;
     bf16* Og = (bf16*)p.out + head + (size_t)qe * D;
+    // this lane's elements of v_0 (4 per block), every load issued before the first is used
+    bf16x4 v0r[NMB];
+    if (V0) {
+#pragma unroll
+      for (int mb = 0; mb < NMB; ++mb) v0r[mb] = *(const bf16x4*)(V0 + 16 * mb + 4 * g);
+    }
 #pragma unroll
     for (int mb = 0; mb < NMB; ++mb) {
       const int d0 = 16 * mb + 4 * g;
@@ -849,7 +855,7 @@ __global__ void __launch_bounds__(512, 4) attn16_kernel(FwdParams p) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         float acc = O[mb][r];
-        if (V0) acc = __builtin_fmaf(w0q, (float)V0[d0 + r], acc);
+        if (V0) acc = __builtin_fmaf(w0q, (float)v0r[mb][r], acc);
         o4[r] = acc * inv;
       }
       *(bf16x4*)(Og + d0) = bf16x4{(bf16)o4[0], (bf16)o4[1], (bf16)o4[2], (bf16)o4[3]};

@@ -541,6 +541,11 @@ __global__ void __launch_bounds__(512, 2) bwd_dq_kernel(BwdParams p) {
   if (qr < Tn) {
     const bf16* k0v = p.k0 ? (const bf16*)p.k0 + (size_t)bh * D : nullptr;
     bf16* out = (bf16*)p.dq + head + (size_t)qr * D;
+    bf16x4 k0r[NMB];  // this lane's elements of k_0, every load issued before the first is used
+    if (k0v) {
+#pragma unroll
+      for (int mb = 0; mb < NMB; ++mb) k0r[mb] = *(const bf16x4*)(k0v + 16 * mb + 4 * g);
+    }
 #pragma unroll
     for (int mb = 0; mb < NMB; ++mb) {
       const int d0 = 16 * mb + 4 * g;
@@ -548,7 +553,7 @@ __global__ void __launch_bounds__(512, 2) bwd_dq_kernel(BwdParams p) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         o4[r] = acc[mb][r];
-        if (k0v) o4[r] = __builtin_fmaf(ds0q, (float)k0v[d0 + r], o4[r]);
+        if (k0v) o4[r] = __builtin_fmaf(ds0q, (float)k0r[mb][r], o4[r]);
       }
       *(bf16x4*)(out + d0) = bf16x4{(bf16)o4[0], (bf16)o4[1], (bf16)o4[2], (bf16)o4[3]};
     }
@@ -634,6 +639,11 @@ __global__ void __launch_bounds__(512, 2) bwd_dq_from_ds_kernel(BwdParams p) {
   const float ds0 = ws.ds0[(size_t)bh * Tn + qr];
   const bf16* k0v = p.k0 ? (const bf16*)p.k0 + (size_t)bh * D : nullptr;
   bf16* out = (bf16*)p.dq + head + (size_t)qr * D;
+  bf16x4 k0r[NMB];  // this lane's elements of k_0, every load issued before the first is used
+  if (k0v) {
+#pragma unroll
+    for (int mb = 0; mb < NMB; ++mb) k0r[mb] = *(const bf16x4*)(k0v + 16 * mb + 4 * g);
+  }
 #pragma unroll
   for (int mb = 0; mb < NMB; ++mb) {
     const int d0 = 16 * mb + 4 * g;
@@ -641,7 +651,7 @@ __global__ void __launch_bounds__(512, 2) bwd_dq_from_ds_kernel(BwdParams p) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       o4[r] = acc[mb][r];
-      if (k0v) o4[r] = __builtin_fmaf(ds0, (float)k0v[d0 + r], o4[r]);
+      if (k0v) o4[r] = __builtin_fmaf(ds0, (float)k0r[mb][r], o4[r]);
     }
     *(bf16x4*)(out + d0) = bf16x4{(bf16)o4[0], (bf16)o4[1], (bf16)o4[2], (bf16)o4[3]};
   }

@@ -361,10 +361,13 @@ __global__ void __launch_bounds__(64 * kDec16Waves, 2) decode16_kernel(DecParams
     l += w0q;
     if (p.v0 != nullptr) {
       const bf16* V0 = (const bf16*)p.v0 + (size_t)bh * D;
+      bf16x4 v0r[NMB];  // every load issued before the first is used
+#pragma unroll
+      for (int mb = 0; mb < NMB; ++mb) v0r[mb] = *(const bf16x4*)(V0 + 16 * mb + 4 * g);
 #pragma unroll
       for (int mb = 0; mb < NMB; ++mb)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) O[mb][r] = __builtin_fmaf(w0q, (float)V0[16 * mb + 4 * g + r], O[mb][r]);
+        for (int r = 0; r < 4; ++r) O[mb][r] = __builtin_fmaf(w0q, (float)v0r[mb][r], O[mb][r]);
     }
   }
   if (n < Tq) {

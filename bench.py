@@ -130,30 +130,67 @@ OTHER_CONFIGS = (("long", 32, 40), ("stress", 16, 80))
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn16_lm_B4H16T4096d128_hbm_traffic.txt")
 
 
-def measured_traffic(workload_name):
-    """HBM bytes per csa_forward launch from the committed rocprofv3 FETCH_SIZE/WRITE_SIZE
-    summary, or None when the workload differs or the kernel sources have changed since
-    the counters were taken (sha256 recorded in the summary)."""
+def _profile_values(path):
+    """The `key = value` lines of a committed rocprofv3 summary, or None when the file is
+    missing or the kernel sources it names have changed since the counters were taken (their
+    sha256 is recorded in the summary)."""
     import hashlib
 
-    if workload_name != "lm" or not os.path.exists(TRAFFIC_FILE):
+    if not os.path.exists(path):
         return None
+    import re
+
     kv = {}
-    with open(TRAFFIC_FILE) as f:
+    with open(path) as f:
         for line in f:
-            if "=" in line and not line.lstrip().startswith("#"):
-                key, val = line.split("=", 1)
-                kv[key.strip()] = val.strip()
+            m = re.match(r"([a-z0-9_]+) = (.*)$", line.strip())
+            if m:
+                kv[m.group(1)] = m.group(2).strip()
     h = hashlib.sha256()
     for rel in kv.get("kernel_sources", "").split():
-        path = os.path.join(ROOT, rel)
-        if not os.path.exists(path):
+        src = os.path.join(ROOT, rel)
+        if not os.path.exists(src):
             return None
-        with open(path, "rb") as f:
+        with open(src, "rb") as f:
             h.update(f.read())
     if h.hexdigest() != kv.get("kernel_source_sha256"):
         return None
+    return kv
+
+
+def measured_traffic(workload_name):
+    """HBM bytes per csa_forward launch from the committed rocprofv3 FETCH_SIZE/WRITE_SIZE
+    summary (lm only), or None when it does not apply to the current kernel."""
+    kv = _profile_values(TRAFFIC_FILE) if workload_name == "lm" else None
+    if kv is None:
+        return None
     return int(kv["csa_fetch_bytes"]) + int(kv["csa_write_bytes"])
+
+
+ISSUE_FILE = os.path.join(ROOT, "profiles", "attn16_lm_B4H16T4096d128_issue_counters.md")
+# Plain VALU issue peak of the chip: 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz, one unpacked
+# fp32 operation per lane and cycle (a wave64 instruction takes a SIMD for 4 cycles); the
+# transcendentals (exp, rcp) issue at a quarter of that rate.
+VALU_PEAK_LANE_OPS = 256 * 4 * 16 * 2.4e9
+
+
+def measured_valu(workload_name, avg_ms):
+    """VALU issue of the csa_forward kernel from the committed SQ_INSTS_* counters (lm only):
+    lane operations per second against the plain VALU peak, with the transcendentals counted
+    once (`frac`) and at their quarter rate (`frac_trans_weighted`), or None when the counters
+    do not apply to the current kernel."""
+    kv = _profile_values(ISSUE_FILE) if workload_name == "lm" else None
+    if kv is None:
+        return None
+    valu = int(kv["csa_insts_valu"]) - int(kv["csa_insts_mfma"])  # wave instructions besides MFMA
+    trans = int(kv["csa_insts_trans"])
+    secs = avg_ms * 1e-3
+    ops = 64.0 * valu / secs
+    weighted = 64.0 * (valu + 3 * trans) / secs
+    return {"bound": "alu", "insts_per_launch": valu, "transcendental_per_launch": trans,
+            "achieved": round(ops / 1e12, 2), "peak": round(VALU_PEAK_LANE_OPS / 1e12, 2),
+            "unit": "T lane-ops/s", "frac": round(ops / VALU_PEAK_LANE_OPS, 4),
+            "frac_trans_weighted": round(weighted / VALU_PEAK_LANE_OPS, 4)}
 
 
 # ------------------------------------------------------------------ GPU leg
@@ -463,6 +500,7 @@ def main():
             "frac": round(tflops / peak, 4),
             "traffic": measured_traffic(w.name),
         },
+        "valu": measured_valu(w.name, avg_ms),
     }
     if not args.no_std:
         sout = torch.empty_like(qd)

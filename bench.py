@@ -169,16 +169,17 @@ def measured_traffic(workload_name):
 
 ISSUE_FILE = os.path.join(ROOT, "profiles", "attn16_lm_B4H16T4096d128_issue_counters.md")
 # Plain VALU issue peak of the chip: 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz, one unpacked
-# fp32 operation per lane and cycle (a wave64 instruction takes a SIMD for 4 cycles); the
-# transcendentals (exp, rcp) issue at a quarter of that rate.
+# fp32 operation per lane and cycle (a wave64 instruction takes a SIMD for 4 cycles).  The
+# SIMD probes measure an exp or rcp at about three times an FMA's issue time.
 VALU_PEAK_LANE_OPS = 256 * 4 * 16 * 2.4e9
+TRANS_ISSUE_WEIGHT = 3
 
 
 def measured_valu(workload_name, avg_ms):
     """VALU issue of the csa_forward kernel from the committed SQ_INSTS_* counters (lm only):
     lane operations per second against the plain VALU peak, with the transcendentals counted
-    once (`frac`) and at their quarter rate (`frac_trans_weighted`), or None when the counters
-    do not apply to the current kernel."""
+    once (`frac`) and at their measured issue cost (`frac_trans_weighted`), or None when the
+    counters do not apply to the current kernel."""
     kv = _profile_values(ISSUE_FILE) if workload_name == "lm" else None
     if kv is None:
         return None
@@ -186,7 +187,7 @@ def measured_valu(workload_name, avg_ms):
     trans = int(kv["csa_insts_trans"])
     secs = avg_ms * 1e-3
     ops = 64.0 * valu / secs
-    weighted = 64.0 * (valu + 3 * trans) / secs
+    weighted = 64.0 * (valu + (TRANS_ISSUE_WEIGHT - 1) * trans) / secs
     return {"bound": "alu", "insts_per_launch": valu, "transcendental_per_launch": trans,
             "achieved": round(ops / 1e12, 2), "peak": round(VALU_PEAK_LANE_OPS / 1e12, 2),
             "unit": "T lane-ops/s", "frac": round(ops / VALU_PEAK_LANE_OPS, 4),

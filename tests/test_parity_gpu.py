@@ -258,6 +258,30 @@ def test_invalid_arguments_raise_on_gpu():
     assert e.value.status == csa.CSA_ERR_INVALID_ARG
 
 
+@pytest.mark.parametrize("rule", ["exact", "half_interval"])
+def test_longest_sequence_sampled_rows(rule):
+    # T = 131072 (one head): the causal index space (T^2 / 2 pairs, 2^33) passes 32 bits, a
+    # key row offset T d reaches 2^24 elements; sampled rows against the oracle, and for every
+    # row the finiteness and convex-combination bounds
+    from oracle import csa_half_reference
+    fn, ref = {"exact": (csa.csa_forward, csa_reference),
+               "half_interval": (csa.csa_forward_half_interval, csa_half_reference)}[rule]
+    T, d = 131072, 128
+    q, k, v, k0, v0 = _random_case(1, 1, T, d, torch.bfloat16, seed=131, sink=True)
+    o_dev, lse_dev = fn(*_gpu(q, k, v, k0, v0))
+    torch.cuda.synchronize()
+    assert bool(torch.isfinite(lse_dev).all()) and bool(torch.isfinite(o_dev.float()).all())
+    vmax = max(float(v.float().abs().max()), float(v0.float().abs().max()))
+    assert float(o_dev.float().abs().max()) <= vmax * (1 + 1e-2)
+    rows = sample_rows(T, seed=131, n_random=6)
+    o = o_dev[:, :, rows].float().cpu().double().numpy()
+    lse = lse_dev[:, :, rows].cpu().double().numpy()
+    o_ref, l_ref = ref(q, k, v, k0, v0, rows=rows)
+    eo, el = _errs(o, lse, o_ref, l_ref)
+    _report(f"T = {T} {rule} ({len(rows)} rows)", eo, el)
+    assert eo <= TOL[torch.bfloat16] and el <= TOL[torch.bfloat16]
+
+
 @pytest.mark.parametrize("name", ["lm", "long", "stress"])
 def test_large_workloads_sampled_rows(name):
     w = WORKLOADS[name]

@@ -75,9 +75,12 @@ struct BwdParams {
 };
 
 // dS tiles for the dq product: for every (b, h), query block qb (128 rows) and key tile
-// kb <= min(2 qb + 1, nkt - 1), 8 waves x 64 lanes x 16 bf16 -- each lane's 16 consecutive
-// keys of its query in the order of the dq product's B operand; qb (qb + 1) tiles precede
-// block qb.
+// kb <= min(2 qb + 1, nkt - 1), 8 waves x 2 halves x 64 lanes x 8 bf16 -- each lane's 16
+// consecutive keys of its query in the order of the dq product's B operand, the 8 keys of
+// half h of every lane of a wave in one contiguous KiB (byte 2048 wave + 1024 h + 16 lane), so
+// that each 16-byte load or store of a wave covers one KiB; qb (qb + 1) tiles precede block qb.
+// (With each lane's 32 bytes together every 16-byte store of bwd_dkdv touched a 2 KiB span at
+// half density; this layout made bwd_dkdv about 2% faster.)
 constexpr int kDsTileBytes = 8 * 64 * 32;
 __device__ __forceinline__ int64_t ds_tile_index(int qb, int kb) { return (int64_t)qb * (qb + 1) + kb; }
 
@@ -598,7 +601,7 @@ __global__ void __launch_bounds__(512, 2) bwd_dq_from_ds_kernel(BwdParams p) {
   const size_t head = (size_t)bh * (size_t)Tn * D;
   const char* Kg = (const char*)((const bf16*)p.k + head);
   const char* dsl = p.ds + ((size_t)bhl * (size_t)p.ds_tiles + (size_t)ds_tile_index(qb, 0)) * kDsTileBytes +
-                    (size_t)(wave * 64 + lane) * 32;
+                    (size_t)(wave * 2048 + lane * 16);
   const int toff = tr_layout_src<ROWB>(tid);
   int vbase[2];
   tr_vbase(n, g, vbase);
@@ -610,7 +613,7 @@ __global__ void __launch_bounds__(512, 2) bwd_dq_from_ds_kernel(BwdParams p) {
   auto load_ds = [&](int j, bf16x8 (&b)[2]) {
     const char* src = dsl + (size_t)j * kDsTileBytes;
     b[0] = *(const bf16x8*)src;
-    b[1] = *(const bf16x8*)(src + 16);
+    b[1] = *(const bf16x8*)(src + 1024);
   };
   if (jw >= 0) load_ds(0, bc);
   stage_tile<D>(lds, Kg, 0, toff, Tn, wave);
@@ -893,7 +896,7 @@ __global__ void __launch_bounds__(512, 4) bwd_dkdv_kernel(BwdParams p) {
       *(CSA_LDS bf16x8*)(lds + OFF_DS + at) = dv;
       if constexpr (WRITE_DS)  // uniform tile base, 32-bit lane offset
         *(bf16x8*)(p.ds + ((size_t)bhl * (size_t)p.ds_tiles + (size_t)ds_tile_index(it, kb)) * kDsTileBytes +
-                   ((wave * 64 + lane) * 32 + 16 * h)) = dv;
+                   (wave * 2048 + h * 1024 + lane * 16)) = dv;
     };
     // every edge exists for every query of the wave, and no row of the wave lies past T
     // (those rows must contribute zeros to dK and dV)

@@ -112,7 +112,8 @@ __device__ __forceinline__ void edge_yu(float pl, float pr, float y, float u, fl
 // roundings (up to 1 ulp each) into a relative error of about 1e-6 / y^2 on R and L, at most
 // 3.3e-3 at |y| = 0.02 in a float32 emulation, which is under the bf16 rounding (up to 2^-8
 // relative) that every weight takes before the P V product.  Such small neighbour differences
-// are rare at the logit scales of attention, so most waves skip the series on most keys.
+// are rare at the logit scales of attention (about 1% of elements), so a wave skips the series
+// on about half of its key steps (64 lanes decide together).
 constexpr float kY0Ballot = 0.02f;
 __device__ __forceinline__ void edge_yu_ballot(float pl, float pr, float y, float u, float Lprev,
                                                float& w_left, float& L_right) {

@@ -60,7 +60,7 @@ def _gpu(*ts):
     return [None if t is None else t.to(DEV) for t in ts]
 
 
-FWD_CASES = _draw_cases(12, seed=20261)
+FWD_CASES = _draw_cases(36, seed=20261)
 RULES = {
     "exact": (csa.csa_forward, csa_reference),
     "first_order": (csa.csa_forward_first_order, csa1_reference),
@@ -87,7 +87,7 @@ def test_forward_random_shapes(case, rule):
     assert eo <= tol and el <= tol, (eo, el)
 
 
-BWD_CASES = _draw_cases(8, seed=20262)
+BWD_CASES = _draw_cases(16, seed=20262)
 
 
 @pytest.mark.parametrize("case", BWD_CASES, ids=lambda c: "c{}-B{}H{}T{}d{}-{}-x{:g}".format(*c))

@@ -407,8 +407,8 @@ def main():
     global SETTLE_S
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="lm")
     ap.add_argument("--settle-s", type=float, default=SETTLE_S,
                     help="untimed warm-up per leg lasts at least this long (GPU clock ramp)")

@@ -122,16 +122,21 @@ __device__ __forceinline__ void edge_yu_ballot(float pl, float pr, float y, floa
   L_right = __builtin_fmaf(kLn2, pr, -du) * u;
   const bool small = __builtin_fabsf(y) < kY0Ballot;
   if (__builtin_amdgcn_ballot_w64(small) != 0) {
-    // an opaque copy of y keeps the series inside the branch (otherwise it is hoisted above
-    // it and the branch becomes two selects on every key)
-    float ys = y;
-    asm volatile("" : "+v"(ys));
-    float gp, gm;
-    Taylor<false>::eval(ys, gp, gm);
-    const float wt = __builtin_fmaf(pl, gp, Lprev);
-    const float lt = pr * gm;
-    w_left = small ? wt : w_left;
-    L_right = small ? lt : L_right;
+    // the lanes that need the series overwrite the closed form under the execution mask (no
+    // selects); the wave-uniform test in front skips the block, with no change of the mask,
+    // when no lane needs it (a plain divergent branch changed the mask on every key: slower
+    // where the series is rare); the empty asm keeps the compiler from folding the two tests
+    // into one divergent branch
+    asm volatile("");
+    if (small) {
+      float gp, gm;
+      Taylor<false>::eval(y, gp, gm);
+      // written into the registers of the closed form (tied operands): as plain code the
+      // compiler formed the first in Lprev's register and copied it over
+      asm("v_fma_f32 %0, %2, %3, %4\n\tv_mul_f32 %1, %5, %6"
+          : "+v"(w_left), "+v"(L_right)
+          : "v"(pl), "v"(gp), "v"(Lprev), "v"(pr), "v"(gm));
+    }
   }
 }
 
@@ -354,6 +359,9 @@ __global__ void __launch_bounds__(512, 4) attn16_kernel(FwdParams p) {
   auto from_lane = [&](int src, float x) {  // value of x in lane src
     return __int_as_float(__builtin_amdgcn_ds_bpermute(src << 2, __float_as_int(x)));
   };
+  auto from_addr = [&](int addr, float x) {
+    return __int_as_float(__builtin_amdgcn_ds_bpermute(addr, __float_as_int(x)));
+  };
   // lanes of the same query in the next / previous lane group, formed where used from the
   // lane index (kept live across the tile loop they were spilled to scratch)
   auto lane_dn = [&]() {
@@ -368,6 +376,15 @@ __global__ void __launch_bounds__(512, 4) attn16_kernel(FwdParams p) {
     asm volatile("" : "+v"(r));
     return r;
   };
+
+  // ds_bpermute byte addresses of the lane of the same query in the next / previous lane group
+  // and of lane n (group 0): formed once and kept across the tile loop (10 VALU per tile fewer
+  // than forming them at each use), except for the interval variant, whose registers they would
+  // push into scratch
+  const int addr_dn_k = ((lane + 16) & 63) << 2, addr_up_k = ((lane + 48) & 63) << 2, addr_n_k = n << 2;
+  auto addr_dn = [&]() { return W == kHalf ? lane_dn() << 2 : addr_dn_k; };
+  auto addr_up = [&]() { return W == kHalf ? lane_up() << 2 : addr_up_k; };
+  auto addr_n = [&]() { return W == kHalf ? (lane_here() & 15) << 2 : addr_n_k; };
 
   // this lane's query slot k of `parked`, addressed from the lane index where used
   auto park = [&](int k) -> CSA_LDS float* {
@@ -550,7 +567,7 @@ __global__ void __launch_bounds__(512, 4) attn16_kernel(FwdParams p) {
     }
     float halo = 0.0f;
     if constexpr (CSA && !last) {
-      halo = from_lane(n, Snext[0][0]);  // key 0 of tile j+1 (lane n, g = 0)
+      halo = from_addr(addr_n(), Snext[0][0]);  // key 0 of tile j+1 (lane n, g = 0)
       mx = fmaxf(mx, halo);
     }
     // a0: in a register for the peeled first tile, from `parked` for a diagonal tile 0
@@ -642,8 +659,8 @@ __global__ void __launch_bounds__(512, 4) attn16_kernel(FwdParams p) {
       // the previous tile's key 63 carried by lanes g = 3, or (first tile) position 0;
       // right of key 15 is the next group's key 0, or (g = 3) the halo
       const float lsend = g == 3 ? carry_s : s[15];
-      float left = from_lane(lane_up(), lsend);
-      float right = from_lane(lane_dn(), s[0]);
+      float left = from_addr(addr_up(), lsend);
+      float right = from_addr(addr_dn(), s[0]);
       carry_s = s[15];
       if (first && g == 0) left = a0v;
       if (!last && g == 3) right = halo;
@@ -672,16 +689,14 @@ __global__ void __launch_bounds__(512, 4) attn16_kernel(FwdParams p) {
       const float pv0 = exp2_fast(al0);
       const float al15 = alpha(15);
       const float pv15 = exp2_fast(al15);
-      // right neighbour of key 15: the next group's key 0, or (g = 3) the halo
-      float ar = from_lane(lane_dn(), al0);
-      float pr = from_lane(lane_dn(), pv0);
-      if (!last) {
-        const float ah = __builtin_fmaf(halo, kLog2e, -mr);
-        if (g == 3) {
-          ar = ah;
-          pr = exp2_fast(ah);
-        }
-      }
+      // right neighbour of key 15: the next group's key 0, or (g = 3) the halo; its logit is
+      // fetched and its exponential formed here in every lane (the halo's is needed anyway, and
+      // an exponential costs no more issue than a second lane exchange and two selects; the
+      // bits are those the neighbouring lane forms for its key 0)
+      float sr = from_addr(addr_dn(), s[0]);
+      if (!last && g == 3) sr = halo;
+      const float ar = __builtin_fmaf(sr, kLog2e, -mr);
+      const float pr = exp2_fast(ar);
       float R15, Lnext;
       if constexpr (last) {
         edge_terms<false>(al15, pv15, ar, pr, R15, Lnext);
@@ -692,7 +707,7 @@ __global__ void __launch_bounds__(512, 4) attn16_kernel(FwdParams p) {
       // left term of key 0: from the previous group, or (g = 0) carried from the
       // previous tile's group 3, or (first tile) from the edge with position 0
       const float Lsend = g == 3 ? carry : Lnext;
-      float Lprev = from_lane(lane_up(), Lsend);
+      float Lprev = from_addr(addr_up(), Lsend);
       carry = Lnext;  // lanes g = 3: left term of key 64(j+1)
       if (first) {    // position 0: only its right neighbour (eq. (10), i = 0)
         const float a0l = __builtin_fmaf(a0v, kLog2e, -mr);

@@ -86,6 +86,37 @@ def test_small_neighbour_differences_bf16(q_mult, d, rule):
     assert eo <= TOL[torch.bfloat16] and el <= TOL[torch.bfloat16]
 
 
+@pytest.mark.parametrize("rule", ["exact", "half_interval"])
+@pytest.mark.parametrize("d", [64, 128])
+def test_series_in_some_lanes_of_a_wave_bf16(d, rule):
+    # queries alternate between logit std ~0.01 (nearly every neighbour difference below the
+    # series threshold) and ~3 (almost none): each wave's 16 queries, one per lane of a lane
+    # group, take the series on some lanes and the closed form on the others at every key step,
+    # so the series is written under a partial execution mask
+    from oracle import csa_half_reference
+    fn, ref = {"exact": (csa.csa_forward, csa_reference),
+               "half_interval": (csa.csa_forward_half_interval, csa_half_reference)}[rule]
+    T = 300
+    q, k, v, k0, v0 = _random_case(1, 3, T, d, torch.float32, seed=6100 + d)
+    scale = torch.where(torch.arange(T) % 2 == 0, torch.tensor(0.01), torch.tensor(3.0))
+    q = (q * scale[None, None, :, None]).to(torch.bfloat16)
+    k, v, k0, v0 = (t.to(torch.bfloat16) for t in (k, v, k0, v0))
+    a = torch.einsum("bhtd,bhsd->bhts", q.double(), k.double())
+    y = (a[..., 1:] - a[..., :-1]).abs() / math.log(2.0)
+    causal = torch.ones(T, T - 1, dtype=torch.bool).tril()
+    small = (y < 0.02) & causal
+    frac_even = float(small[:, :, 0::2].double().sum() / causal[0::2].sum() / 3)
+    frac_odd = float(small[:, :, 1::2].double().sum() / causal[1::2].sum() / 3)
+    assert frac_even > 0.5 and frac_odd < 0.02, (frac_even, frac_odd)
+    o, lse = fn(*_gpu(q, k, v, k0, v0))
+    torch.cuda.synchronize()
+    o, lse = o.float().cpu().double().numpy(), lse.cpu().double().numpy()
+    o_ref, l_ref = ref(q, k, v, k0, v0)
+    eo, el = _errs(o, lse, o_ref, l_ref)
+    _report(f"series on alternate queries d{d} {rule} (small fraction {frac_even:.2f} / {frac_odd:.3f})", eo, el)
+    assert eo <= TOL[torch.bfloat16] and el <= TOL[torch.bfloat16]
+
+
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16], ids=["f32", "bf16"])
 @pytest.mark.parametrize("d", [16, 64, 128])
 @pytest.mark.parametrize("T", [1, 2, 3, 31, 32, 33, 63, 64, 65, 127, 128, 129, 200, 257])

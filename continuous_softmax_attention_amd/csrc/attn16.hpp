@@ -778,7 +778,11 @@ __global__ void __launch_bounds__(512, 4) attn16_kernel(FwdParams p) {
         slot(t);
       }
     }
-    // P V of keys 8..15 of every lane group
+    // P V of keys 8..15 of every lane group, at the highest of the tile's priorities: a wave
+    // that has formed its last weights issues the tile's last products ahead of the other waves'
+    // weight work and reaches the barrier sooner (lm +1.3% to +2.4% in three interleaved A/Bs,
+    // level on long and stress)
+    __builtin_amdgcn_s_setprio(2);
     const bf16x8 P1 = pack(1);
 #pragma unroll
     for (int u = 0; u < NP; ++u) pv_unit(1, u, P1);

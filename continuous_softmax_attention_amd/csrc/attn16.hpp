@@ -534,7 +534,8 @@ __global__ void __launch_bounds__(512, 4) attn16_kernel(FwdParams p) {
     constexpr bool last = decltype(last_c)::value;  // the tile holding this wave's diagonal
     const bool first = decltype(first_c)::value || (last && j == 0);
     // Wave priority 1 while the wave forms the weights of keys 0..7 and issues the next tile's
-    // S^T products, 0 for keys 8..15 and the P V products: a SIMD serves waves that have just
+    // S^T products, 0 for keys 8..15 and the first key chunk's P V products (2 for the second
+    // chunk's, after the weight steps; see there): a SIMD serves waves that have just
     // entered a tile, whose S^T products start the next tile's dependency chain, ahead of waves
     // finishing one.  Interleaved A/B against equal priorities: +2% lm, +3% long, +12% stress
     // (logit std 8); lowering after key 3 or 11, or a priority falling with every four keys
